@@ -1,0 +1,65 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins catch each.
+
+Each mutant is the oracle's source with one textual change (a dropped term, a
+wrong sign, denominator, index or reduction), loaded as a separate module on
+the CPU.  The pins in ``oracle_pins`` must reject every one of them; a mutant
+no pin rejects would mean a part of the oracle is not really pinned.
+"""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "rmsnorm_oracle.py")
+
+MUTANTS = {
+    "denominator_n_plus_1": ("mean_sq = np.sum(x * x, axis=1) / n", "mean_sq = np.sum(x * x, axis=1) / (n + 1)"),
+    "denominator_padded_pow2": ("mean_sq = np.sum(x * x, axis=1) / n",
+                                "mean_sq = np.sum(x * x, axis=1) / (1 << (n - 1).bit_length())"),
+    "rows_for_columns": ("    n = x.shape[1]\n    mean_sq", "    n = x.shape[0]\n    mean_sq"),
+    "eps_outside_root": ("return 1.0 / np.sqrt(mean_sq + eps)", "return 1.0 / np.sqrt(mean_sq) + eps"),
+    "eps_dropped": ("return 1.0 / np.sqrt(mean_sq + eps)", "return 1.0 / np.sqrt(mean_sq)"),
+    "sqrt_not_inverse": ("return 1.0 / np.sqrt(mean_sq + eps)", "return np.sqrt(mean_sq + eps)"),
+    "gemma_ignored": ("return 1.0 + g", "return g"),
+    "gemma_sign": ("return 1.0 + g", "return 1.0 - g"),
+    "forward_drops_weight": ("y = x * r[:, None] * w[None, :]", "y = x * r[:, None]"),
+    "u_drops_weight": ("u = dy * w[None, :]", "u = dy"),
+    "m_wrong_operand": ("m = np.sum(u * x, axis=1) / n", "m = np.sum(u * dy, axis=1) / n"),
+    "m_sum_not_mean": ("m = np.sum(u * x, axis=1) / n", "m = np.sum(u * x, axis=1)"),
+    "m_padded_denominator": ("m = np.sum(u * x, axis=1) / n", "m = np.sum(u * x, axis=1) / (1 << (n - 1).bit_length())"),
+    "bwd_rows_for_columns": ("    n = x.shape[1]\n    r = inverse_rms", "    n = x.shape[0]\n    r = inverse_rms"),
+    "dx_projection_dropped": ("dx = r[:, None] * u - x * (r**3 * m)[:, None]", "dx = r[:, None] * u"),
+    "dx_projection_sign": ("dx = r[:, None] * u - x * (r**3 * m)[:, None]", "dx = r[:, None] * u + x * (r**3 * m)[:, None]"),
+    "dx_r_squared": ("dx = r[:, None] * u - x * (r**3 * m)[:, None]", "dx = r[:, None] * u - x * (r**2 * m)[:, None]"),
+    "dx_direct_term_no_r": ("dx = r[:, None] * u - x * (r**3 * m)[:, None]", "dx = u - x * (r**3 * m)[:, None]"),
+    "dgamma_drops_r": ("dgamma = dgamma_from_rows(dy * x * r[:, None])", "dgamma = dgamma_from_rows(dy * x)"),
+    "dgamma_includes_weight": ("dgamma = dgamma_from_rows(dy * x * r[:, None])",
+                               "dgamma = dgamma_from_rows(dy * x * r[:, None] * w[None, :])"),
+    "dgamma_uses_u": ("dgamma = dgamma_from_rows(dy * x * r[:, None])", "dgamma = dgamma_from_rows(u * x * r[:, None])"),
+    "dgamma_mean_not_sum": ("return np.sum(_f64(contributions), axis=0)", "return np.mean(_f64(contributions), axis=0)"),
+    "dgamma_sums_columns": ("return np.sum(_f64(contributions), axis=0)", "return np.sum(_f64(contributions), axis=1)"),
+}
+
+
+def _load_mutant(name, old, new):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation {name!r} does not match the oracle source exactly once"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(name, *MUTANTS[name])
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # an assertion or a shape error both reject the mutant
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin rejects the mutant {name!r}"
