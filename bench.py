@@ -1,0 +1,278 @@
+"""Benchmark: RMSNorm fwd+bwd achieved HBM GB/s on one MI355X.
+
+One step = the whole path over one batch: forward (y, r), backward row pass
+(dx written in place over dy, per-workgroup dgamma partials) and the dgamma
+column reduction — three launches through the C ABI on torch's current HIP
+stream.  Inputs are seeded synthetic tensors already resident in HBM.  The
+default workload is bf16 M=16384 N=8192 with the Gemma (1+gamma) weight and an
+in-place dx: the configuration the metric is quoted on.
+
+Prints ONE JSON line.  ``value`` is algorithmic bytes of fwd+bwd per step
+divided by the measured step time; ``roofline`` describes the dominant kernel
+(the backward row pass) timed per launch with HIP events on the same stream;
+``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "RMSNorm fwd+bwd achieved HBM GB/s and % of peak, bf16 M=16384 N=8192"
+KERNEL_SRC = os.path.join(ROOT, "row_normalization_amd", "csrc", "rmsnorm_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(h: str):
+    """HBM bytes per backward-row-pass launch from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    m_bytes = re.search(r"scaled HBM bytes per launch:\s*`?([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != h:
+        return None
+    return int(m_bytes.group(1))
+
+
+class Path:
+    """Device buffers and pre-marshalled C-ABI calls for one workload."""
+
+    def __init__(self, w: wl.Workload):
+        import row_normalization_amd as rn
+
+        self.w = w
+        self.L = rn.lib()
+        t = wl.make_inputs(w)
+        dev = "cuda"
+        self.x = t["x"].to(dev)
+        self.gamma = t["gamma"].to(dev)
+        self.dy = t["dy"].to(dev)
+        self.y = torch.empty_like(self.x)
+        self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
+        self.dx = self.dy if w.dx_in_place else torch.empty_like(self.dy)
+        self.dgamma = torch.empty(w.N, dtype=torch.float32, device=dev)
+        self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(w.M, w.N, w.torch_dtype)
+        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device=dev)
+        self.dtype = 0 if w.dtype == "f32" else 1
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.rows = ctypes_int64()
+        self.partial_rows = None
+
+    def fwd(self):
+        st = self.L.rmsnorm_fwd(self.x.data_ptr(), self.gamma.data_ptr(), self.y.data_ptr(), self.rstd.data_ptr(),
+                                self.w.M, self.w.N, self.w.N, self.w.eps, self.dtype, int(self.w.gemma), self.stream)
+        assert st == 0, st
+
+    def bwd_rows(self):
+        st = self.L.rmsnorm_bwd_rows(self.x.data_ptr(), self.gamma.data_ptr(), self.dy.data_ptr(),
+                                     self.rstd.data_ptr(), self.dx.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                                     self.w.M, self.w.N, self.w.N, self.dtype, int(self.w.gemma), self.rows.ref,
+                                     self.stream)
+        assert st == 0, st
+        self.partial_rows = self.rows.value
+
+    def reduce(self):
+        st = self.L.rmsnorm_dgamma_reduce(self.ws.data_ptr(), self.partial_rows, self.w.N, self.dgamma.data_ptr(),
+                                          self.stream)
+        assert st == 0, st
+
+    def step(self):
+        self.fwd()
+        self.bwd_rows()
+        self.reduce()
+
+
+class ctypes_int64:
+    def __init__(self):
+        import ctypes
+
+        self._v = ctypes.c_int64(0)
+        self.ref = ctypes.byref(self._v)
+
+    @property
+    def value(self):
+        return self._v.value
+
+
+def time_steps(path: Path, steps: int) -> float:
+    """Seconds per step over `steps` back-to-back steps (HIP events on the stream)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        path.step()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e-3 / steps
+
+
+def time_kernels(path: Path, steps: int) -> dict:
+    """Average duration of each launch, from events recorded between the launches."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record()
+        path.fwd()
+        ev[k][1].record()
+        path.bwd_rows()
+        ev[k][2].record()
+        path.reduce()
+        ev[k][3].record()
+    torch.cuda.synchronize()
+    names = ["fwd", "bwd_rows", "dgamma_reduce"]
+    out = {}
+    for i, n in enumerate(names):
+        d = [ev[k][i].elapsed_time(ev[k][i + 1]) * 1e-3 for k in range(steps)]
+        out[n] = {"mean_s": float(np.mean(d)), "median_s": float(np.median(d))}
+    return out
+
+
+def copy_reference(nbytes: int, steps: int) -> float:
+    """GB/s of a plain device-to-device copy (read + write counted) of nbytes."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) * 1e-3 / steps
+    return 2 * nbytes / t / 1e9
+
+
+def cpu_baseline(w: wl.Workload, seconds: float) -> dict:
+    """The fp64 oracle (as it stands) on a sample of rows of the same workload."""
+    import oracle
+
+    rows = min(w.M, 1024)
+    sample = w.scaled(M=rows)
+    t = wl.make_inputs(sample)
+    x, g, dy = (wl.to_f64(t[k]) for k in ("x", "gamma", "dy"))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(x, g, w.eps, w.gemma)
+        oracle.backward(x, g, dy, w.eps, w.gemma)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and reps >= 2:
+            break
+    per = el / reps
+    nbytes = wl.algorithmic_bytes(rows, w.N, w.elsize)["fwd_bwd"]
+    return {"value": nbytes / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {w.M} rows x N={w.N} ({w.dtype} inputs upcast to fp64), fwd+bwd repeated {reps}x "
+                      f"in {el:.1f} s; numpy elementwise ops, single thread; {per * 1e3:.1f} ms per sample",
+            "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this path is measured on a single MI355X; "
+              "multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import row_normalization_amd as rn
+
+    if not os.path.exists(rn.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+    w = wl.CONFIGS[args.workload]
+    path = Path(w)
+    for _ in range(max(args.warmup, 1)):
+        path.step()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    sec_per_step = time_steps(path, args.steps)
+    wall = time.perf_counter() - t0
+    kern = time_kernels(path, args.steps)
+
+    b = wl.algorithmic_bytes(w.M, w.N, w.elsize)
+    value = b["fwd_bwd"] / sec_per_step / 1e9
+    t_rows = kern["bwd_rows"]["mean_s"]
+    achieved = b["bwd_rows"] / t_rows / 1e9
+    h = kernel_hash()
+    traffic = traffic_from_profile(h)
+    copy_gbps = copy_reference(256 << 20, 50)
+    props = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "gemma": w.gemma, "dx_in_place": w.dx_in_place,
+                   "eps": w.eps, "io_dtype": w.dtype, "math": "fp32"},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(w.M / sec_per_step, 1),
+        "bytes_per_step": b["fwd_bwd"],
+        "wall_s_timed": round(wall, 4),
+        "kernels_us": {k: round(v["mean_s"] * 1e6, 2) for k, v in kern.items()},
+        "kernels_gbps": {"fwd": round(b["fwd"] / kern["fwd"]["mean_s"] / 1e9, 1),
+                         "bwd_rows": round(achieved, 1),
+                         "bwd": round(b["bwd"] / (kern["bwd_rows"]["mean_s"] + kern["dgamma_reduce"]["mean_s"]) / 1e9,
+                                      1)},
+        "partial_rows": path.partial_rows,
+        "copy_ref_gbps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "rmsnorm_bwd_rows_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": b["bwd_rows"], "kernel_sha": h},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * rmsnorm.h — C ABI of the MI355X (gfx950) fused RMSNorm library.
+ *
+ * Operations, as defined on the Triton RMSNorm tutorial "Hướng dẫn Triton
+ * RMSNorm: kernel, backward và…" (partitech.com) and the Unsloth kernel
+ * walkthrough "02 · 手写 Triton kernel:RMSNorm / RoPE / SwiGLU" (section 3):
+ *
+ *   forward   r_i  = 1 / sqrt(mean_j x_ij^2 + eps)          (eps under the root)
+ *             y_ij = x_ij * r_i * w_j                       (w = gamma, or 1 + gamma
+ *                                                            for the Gemma variant)
+ *   backward  u_ij = dy_ij * w_j,  m_i = mean_j u_ij x_ij
+ *             dx_ij = r_i u_ij - x_ij r_i^3 m_i
+ *             dgamma_j = sum_i dy_ij x_ij r_i               (a sum over rows, not a mean)
+ *
+ * The tutorial splits the backward into a row pass ("backward_rows": dx plus
+ * per-row dgamma contributions) and a column reduction
+ * ("reduce_gamma_gradient"); this library keeps that split as
+ * rmsnorm_bwd_rows + rmsnorm_dgamma_reduce, with the contributions summed per
+ * workgroup first (one fp32 partial row per workgroup instead of one per
+ * matrix row), and rmsnorm_bwd runs both.
+ *
+ * Conventions for every entry point:
+ *  - Matrices are row-major M x N with a row stride (in elements) shared by
+ *    all matrices of one call; elements of a row are contiguous.
+ *  - dtype is RMSNORM_F32 or RMSNORM_BF16 and applies to x, gamma, y, dy and
+ *    dx.  rstd (the saved r) is always fp32[M]; dgamma and the partials are
+ *    always fp32.  Arithmetic is fp32 in registers; each bf16 output is
+ *    rounded once, to nearest even.
+ *  - All pointers are device pointers to memory the caller owns (for example
+ *    PyTorch tensors).  The library allocates nothing and keeps no state
+ *    between calls; calls are asynchronous on `stream` (0 = the null stream)
+ *    and their outputs are valid once the stream has reached them.
+ *  - Arguments are validated on the host before anything is launched.  On any
+ *    error nothing is launched and nothing is written.  Status codes are
+ *    returned, never thrown.  There is no fallback path of any kind.
+ *  - 16-byte vector loads are used when every base pointer, N and the row
+ *    stride allow them; otherwise narrower loads (down to one element) — the
+ *    results are the same either way up to fp32 summation order.
+ *  - Results are deterministic: the same inputs, shapes and pointer
+ *    alignments give bitwise identical outputs on every run (fixed row-to-
+ *    workgroup assignment, fixed summation order, no atomics on data).
+ */
+#ifndef RMSNORM_H
+#define RMSNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RMSNORM_F32 = 0, RMSNORM_BF16 = 1 } rmsnorm_dtype;
+
+typedef enum {
+  RMSNORM_OK = 0,
+  RMSNORM_E_NULL = -1,      /* a required pointer is NULL (only checked when M > 0, or N for dgamma) */
+  RMSNORM_E_SHAPE = -2,     /* M < 0, N < 1, N > RMSNORM_N_MAX, or partial-row count < 0 */
+  RMSNORM_E_STRIDE = -3,    /* row_stride < N */
+  RMSNORM_E_ALIGN = -4,     /* a pointer is not aligned to its element size */
+  RMSNORM_E_DTYPE = -5,     /* dtype is not RMSNORM_F32 / RMSNORM_BF16 */
+  RMSNORM_E_EPS = -6,       /* eps is not finite or not > 0 */
+  RMSNORM_E_ALIAS = -7,     /* an output overlaps another buffer (dx == dy is the one allowed case) */
+  RMSNORM_E_WORKSPACE = -8, /* workspace smaller than rmsnorm_bwd_workspace_bytes() */
+  RMSNORM_E_FLAG = -9,      /* gemma is not 0 or 1 */
+  RMSNORM_E_HIP = -10       /* a HIP launch failed */
+} rmsnorm_status;
+
+/* Largest supported row length (columns). */
+#define RMSNORM_N_MAX 16384
+
+/*
+ * Forward: y = x * r * w and the saved r (tutorial, "Vấn đề và công thức tham
+ * chiếu" and "Forward Triton: một hàng, một chương trình"; Gemma weight from
+ * the Unsloth walkthrough, section 3).
+ *
+ *   x      [M, N] dtype, read         gamma [N] dtype, read
+ *   y      [M, N] dtype, written (every element of the M x N view; the padding
+ *          between rows of a strided view is not touched)
+ *   rstd   [M] fp32, written: r_i, for rmsnorm_bwd_rows
+ *   row_stride  elements between row starts of x and y (>= N)
+ *   eps    finite, > 0; added to the mean of squares under the square root
+ *   gemma  0: w = gamma;  1: w = 1 + gamma (formed in fp32)
+ * M == 0 is a no-op.  y must not overlap x, gamma or rstd.
+ */
+int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M, int64_t N,
+                int64_t row_stride, float eps, int dtype, int gemma, hipStream_t stream);
+
+/*
+ * Size in bytes of the fp32 partials workspace rmsnorm_bwd_rows / rmsnorm_bwd
+ * need for an M x N problem of this dtype (an upper bound on the partial rows
+ * actually written, times N * 4).  Pure host arithmetic, no HIP call.
+ * Returns a status; *bytes is written only on RMSNORM_OK.
+ */
+int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t* bytes);
+
+/*
+ * Backward row pass: dx for every row and the dgamma contributions dy*x*r
+ * summed per workgroup into fp32 partial rows (tutorial, "Backward đầu vào:
+ * giữ đúng N", "Lập phương của r từ đâu?" and "Reduce dgamma không có race
+ * khi ghi").  r is taken from rstd, never recomputed.
+ *
+ *   x, dy  [M, N] dtype, read          gamma [N] dtype, read
+ *   rstd   [M] fp32, read (as written by rmsnorm_fwd with the same x, eps)
+ *   dx     [M, N] dtype, written; may be exactly dy (same pointer) for an
+ *          in-place backward — each element of dy is read before it is
+ *          overwritten, and nothing later reads dy
+ *   workspace  fp32, at least rmsnorm_bwd_workspace_bytes(); on return its
+ *          first (*partial_rows) rows of N floats hold the partial sums
+ *   partial_rows  out: number of partial rows written (0 when M == 0)
+ *   gemma  as in rmsnorm_fwd
+ * dx must not overlap x, gamma, rstd or the workspace, except dx == dy.
+ */
+int rmsnorm_bwd_rows(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx,
+                     void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride,
+                     int dtype, int gemma, int64_t* partial_rows, hipStream_t stream);
+
+/*
+ * Second stage of the weight gradient: dgamma_j = sum over the `rows` partial
+ * rows of partials[p, j], summed in fp32 in a fixed order (tutorial, "Reduce
+ * dgamma không có race khi ghi" and "Tổng không phải trung bình": a sum, no
+ * division by the row count).
+ *
+ *   partials  [rows, N] fp32, row-major and contiguous, read (may be NULL when rows == 0)
+ *   dgamma    [N] fp32, overwritten (rows == 0 gives zeros)
+ */
+int rmsnorm_dgamma_reduce(const float* partials, int64_t rows, int64_t N, float* dgamma, hipStream_t stream);
+
+/*
+ * Full backward: rmsnorm_bwd_rows followed by rmsnorm_dgamma_reduce on the
+ * same stream.  dgamma [N] fp32 is overwritten (zeros when M == 0), never
+ * accumulated into; it must not overlap any other buffer.
+ */
+int rmsnorm_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx, float* dgamma,
+                void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride, int dtype,
+                int gemma, hipStream_t stream);
+
+/* A static, human-readable description of a status code. */
+const char* rmsnorm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_H */

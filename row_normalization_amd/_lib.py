@@ -1,0 +1,191 @@
+"""ctypes binding of ``librmsnorm.so`` (the C ABI in ``include/rmsnorm.h``).
+
+Argument marshalling only: tensors are turned into device pointers, shapes,
+row strides, a dtype code and the current HIP stream, and the C status is
+turned into an exception.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library has not been built, or a tensor
+is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "librmsnorm.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "rmsnorm.h")
+
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+STATUS = {
+    0: "RMSNORM_OK", -1: "RMSNORM_E_NULL", -2: "RMSNORM_E_SHAPE", -3: "RMSNORM_E_STRIDE", -4: "RMSNORM_E_ALIGN",
+    -5: "RMSNORM_E_DTYPE", -6: "RMSNORM_E_EPS", -7: "RMSNORM_E_ALIAS", -8: "RMSNORM_E_WORKSPACE",
+    -9: "RMSNORM_E_FLAG", -10: "RMSNORM_E_HIP",
+}
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+_SIGNATURES = {
+    "rmsnorm_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int,
+                                   ctypes.c_int, _c_p]),
+    "rmsnorm_bwd_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "rmsnorm_bwd_rows": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64, _c_i64, _c_i64,
+                                        ctypes.c_int, ctypes.c_int, ctypes.POINTER(_c_i64), _c_p]),
+    "rmsnorm_dgamma_reduce": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
+    "rmsnorm_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64, _c_i64, _c_i64,
+                                   ctypes.c_int, ctypes.c_int, _c_p]),
+    "rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+class RMSNormError(RuntimeError):
+    """A HIP launch failure reported by the library."""
+
+
+def header_functions() -> list[str]:
+    """Names of the functions ``include/rmsnorm.h`` declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"^(?:int|const char\*)\s+(rmsnorm_\w+)\s*\(", text, flags=re.M)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m row_normalization_amd.build` "
+                               "(there is no fallback implementation)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def rmsnorm_status_string(status: int) -> str:
+    return lib().rmsnorm_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status == 0:
+        return
+    msg = f"{what}: {STATUS.get(status, status)} ({rmsnorm_status_string(status)})"
+    if status == -10:
+        raise RMSNormError(msg)
+    raise ValueError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}; the library takes float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("the RMSNorm library takes GPU tensors only (no CPU path)")
+
+
+def _rows(t: torch.Tensor, name: str) -> tuple[int, int, int]:
+    """(M, N, row_stride) of a 2-D view whose rows are contiguous."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [M, N]")
+    M, N = t.shape
+    if N > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows (stride(1) == 1)")
+    return M, N, t.stride(0) if M > 1 else max(N, t.stride(0))
+
+
+def _same_layout(ref: torch.Tensor, other: torch.Tensor, name: str, stride: int) -> None:
+    if other.shape != ref.shape or other.dtype != ref.dtype:
+        raise ValueError(f"{name} must match x in shape and dtype")
+    if other.shape[0] > 1 and other.stride(0) != stride:
+        raise ValueError(f"{name} must share x's row stride ({stride})")
+    if other.shape[1] > 1 and other.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def rmsnorm_fwd(x, gamma, y, rstd, eps: float = 1e-6, gemma: bool = False, stream=None) -> None:
+    """y = x * r * w and rstd = r (w = gamma, or 1 + gamma with ``gemma``), on the GPU."""
+    _gpu(x, gamma, y, rstd)
+    M, N, stride = _rows(x, "x")
+    _same_layout(x, y, "y", stride)
+    if rstd.dtype != torch.float32 or rstd.numel() != M or (M > 1 and rstd.stride(0) != 1):
+        raise ValueError("rstd must be a contiguous float32 tensor of M elements")
+    st = lib().rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, stride, float(eps), _dtype_code(x),
+                           int(bool(gemma)), _stream(stream))
+    _check(st, "rmsnorm_fwd")
+
+
+def rmsnorm_bwd_workspace_bytes(M: int, N: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DTYPES.get(dtype, -1)
+    out = ctypes.c_size_t(0)
+    _check(lib().rmsnorm_bwd_workspace_bytes(int(M), int(N), int(code), ctypes.byref(out)),
+           "rmsnorm_bwd_workspace_bytes")
+    return int(out.value)
+
+
+def _bwd_checks(x, gamma, dy, rstd, dx):
+    _gpu(x, gamma, dy, rstd, dx)
+    M, N, stride = _rows(x, "x")
+    _same_layout(x, dy, "dy", stride)
+    _same_layout(x, dx, "dx", stride)
+    if rstd.dtype != torch.float32 or rstd.numel() != M:
+        raise ValueError("rstd must be float32 with M elements")
+    return M, N, stride
+
+
+def rmsnorm_bwd_rows(x, gamma, dy, rstd, dx, workspace, gemma: bool = False, stream=None) -> int:
+    """dx (may be dy itself) and per-workgroup dgamma partial rows; returns the partial-row count."""
+    M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
+    _gpu(workspace)
+    rows = _c_i64(0)
+    st = lib().rmsnorm_bwd_rows(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), M, N, stride, _dtype_code(x),
+                                int(bool(gemma)), ctypes.byref(rows), _stream(stream))
+    _check(st, "rmsnorm_bwd_rows")
+    return int(rows.value)
+
+
+def rmsnorm_dgamma_reduce(partials, rows: int, N: int, dgamma, stream=None) -> None:
+    """dgamma[j] = sum of the first ``rows`` rows of the [rows, N] fp32 partials."""
+    _gpu(partials, dgamma)
+    if dgamma.dtype != torch.float32 or dgamma.numel() != N:
+        raise ValueError("dgamma must be float32 with N elements")
+    if partials is not None and partials.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    st = lib().rmsnorm_dgamma_reduce(_ptr(partials), int(rows), int(N), _ptr(dgamma), _stream(stream))
+    _check(st, "rmsnorm_dgamma_reduce")
+
+
+def rmsnorm_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, gemma: bool = False, stream=None) -> None:
+    """Full backward: dx (may be dy itself) and dgamma (fp32, overwritten)."""
+    M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
+    _gpu(dgamma, workspace)
+    if dgamma.dtype != torch.float32 or dgamma.numel() != N:
+        raise ValueError("dgamma must be float32 with N elements")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
+                           wbytes, M, N, stride, _dtype_code(x), int(bool(gemma)), _stream(stream))
+    _check(st, "rmsnorm_bwd")

@@ -1,0 +1,62 @@
+"""Build ``librmsnorm.so`` (gfx950 kernels + host C ABI) in-tree.
+
+``python -m row_normalization_amd.build`` or ``build()``.  The host TU
+(validation, planning, entry points) is compiled by g++, the kernels by hipcc
+for gfx950 only; hipcc links both into one shared library next to this file.
+Packed fp32 vector instructions are disabled in device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "librmsnorm.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # no packed-fp32 (v_pk_*_f32) instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _run(cmd: list[str]) -> None:
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if out.strip():
+        print(out)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile the library; returns its path.  Always recompiles."""
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    os.makedirs(BUILD, exist_ok=True)
+    api_o = os.path.join(BUILD, "rmsnorm_api.o")
+    ker_o = os.path.join(BUILD, "rmsnorm_kernels.o")
+    tmp = LIB + ".tmp"
+    steps = [
+        ["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+         f"-I{INCLUDE}", f"-I{os.path.join(ROCM, 'include')}", "-c", os.path.join(CSRC, "rmsnorm_api.cpp"), "-o", api_o],
+        [hipcc, *HIP_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, "rmsnorm_kernels.hip"), "-o", ker_o],
+        [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, ker_o, "-o", tmp],
+    ]
+    for cmd in steps:
+        if verbose:
+            print("+", " ".join(cmd), flush=True)
+        _run(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-q" not in sys.argv))
