@@ -160,6 +160,30 @@ def time_kernels(path: Path, steps: int) -> dict:
     return out
 
 
+def time_cold(path: Path, samples: int) -> dict:
+    """Each launch timed alone after a 1 GiB write has pushed the previous data
+    out of L2 and the 256 MB Infinity Cache (medians over `samples`).  Nothing
+    a launch reads is then cached from an earlier launch, except the dgamma
+    partials the row pass has just written for the reduction."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(samples)]
+    torch.cuda.synchronize()
+    for k in range(samples):
+        flush.fill_(float(k))
+        ev[k][0].record()
+        path.fwd()
+        ev[k][1].record()
+        flush.fill_(float(k) + 0.5)
+        ev[k][2].record()
+        path.bwd_rows()
+        ev[k][3].record()
+        path.reduce()
+        ev[k][4].record()
+    torch.cuda.synchronize()
+    med = lambda a, b: float(np.median([ev[k][a].elapsed_time(ev[k][b]) * 1e-3 for k in range(samples)]))
+    return {"fwd": med(0, 1), "bwd_rows": med(2, 3), "dgamma_reduce": med(3, 4)}
+
+
 def copy_reference(nbytes: int, steps: int) -> float:
     """GB/s of a plain device-to-device copy (read + write counted) of nbytes."""
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -227,6 +251,7 @@ def main():
     sec_per_step = time_steps(path, args.steps)
     wall = time.perf_counter() - t0
     kern = time_kernels(path, args.steps)
+    cold = time_cold(path, max(10, min(args.steps, 50)))
 
     b = wl.algorithmic_bytes(w.M, w.N, w.elsize)
     value = b["fwd_bwd"] / sec_per_step / 1e9
@@ -260,6 +285,11 @@ def main():
                          "bwd_rows": round(achieved, 1),
                          "bwd": round(b["bwd"] / (kern["bwd_rows"]["mean_s"] + kern["dgamma_reduce"]["mean_s"]) / 1e9,
                                       1)},
+        "cold": {"kernels_us": {k: round(v * 1e6, 2) for k, v in cold.items()},
+                 "ms_per_step": round(sum(cold.values()) * 1e3, 4),
+                 "gbps": round(b["fwd_bwd"] / sum(cold.values()) / 1e9, 1),
+                 "bwd_rows_gbps": round(b["bwd_rows"] / cold["bwd_rows"] / 1e9, 1),
+                 "fwd_gbps": round(b["fwd"] / cold["fwd"] / 1e9, 1)},
         "partial_rows": path.partial_rows,
         "copy_ref_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "rmsnorm_bwd_rows_kernel", "achieved": round(achieved, 1),

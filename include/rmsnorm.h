@@ -57,7 +57,8 @@ typedef enum { RMSNORM_F32 = 0, RMSNORM_BF16 = 1 } rmsnorm_dtype;
 typedef enum {
   RMSNORM_OK = 0,
   RMSNORM_E_NULL = -1,      /* a required pointer is NULL (only checked when M > 0, or N for dgamma) */
-  RMSNORM_E_SHAPE = -2,     /* M < 0, N < 1, N > RMSNORM_N_MAX, or partial-row count < 0 */
+  RMSNORM_E_SHAPE = -2,     /* M outside [0, RMSNORM_M_MAX], N outside [1, RMSNORM_N_MAX], or a bad
+                               partials table (rows < 0 or rows * N > RMSNORM_PARTIALS_MAX) */
   RMSNORM_E_STRIDE = -3,    /* row_stride < N */
   RMSNORM_E_ALIGN = -4,     /* a pointer is not aligned to its element size */
   RMSNORM_E_DTYPE = -5,     /* dtype is not RMSNORM_F32 / RMSNORM_BF16 */
@@ -68,8 +69,12 @@ typedef enum {
   RMSNORM_E_HIP = -10       /* a HIP launch failed */
 } rmsnorm_status;
 
-/* Largest supported row length (columns). */
+/* Largest supported row length (columns), row count, and partials table
+ * (rows * N floats) accepted by rmsnorm_dgamma_reduce.  The kernels address
+ * a row, the saved r and the partials through 32-bit byte offsets. */
 #define RMSNORM_N_MAX 16384
+#define RMSNORM_M_MAX (1LL << 29)
+#define RMSNORM_PARTIALS_MAX (1LL << 29)
 
 /*
  * Forward: y = x * r * w and the saved r (tutorial, "Vấn đề và công thức tham

@@ -74,10 +74,10 @@ struct ReduceArgs {
 constexpr int kItersSet[] = {1, 2, 4, 5, 8, 16};
 constexpr int kItersMax = 16;
 
-// Column tile of the dgamma reduction: kReduceCols column-threads x
-// kReduceSlices row slices per 256-thread block.
-constexpr int kReduceCols = 16;
-constexpr int kReduceSlices = 16;
+// Tile of the dgamma reduction: kReduceCols column threads (a 128-byte row
+// segment with 16-byte loads) x kReduceSlices row slices per 256-thread block.
+constexpr int kReduceCols = 8;
+constexpr int kReduceSlices = 32;
 
 // dtype codes match rmsnorm_dtype.  Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(int dtype, const RowPlan& p, const FwdArgs& a, hipStream_t s);

@@ -15,21 +15,32 @@
 namespace rmsn {
 namespace {
 
-// Persistent grid of the backward row pass: one 1024-thread workgroup per
-// compute unit of an MI355X (256 CUs).
-constexpr int64_t kBwdGrid = 256;
+// Launch shape.  A row group spans as many waves as it takes for each lane
+// to hold kLaneVectors 16-byte vectors of every row operand; workgroups hold
+// about kBlockWaves waves (several row groups when rows are short).  Measured
+// on MI355X at M=16384, N=8192 bf16: two vectors per lane and eight waves per
+// row beat both fewer, fatter lanes and whole-row-per-wave layouts, for the
+// forward and the backward alike.
+constexpr int kLaneVectors = 2;
+constexpr int kBlockWaves = 8;
+// The backward grid is persistent: a whole number of workgroups on each of
+// the 256 compute units (a power of two, so that every CU gets the same
+// count), about kBwdResidentWaves waves per CU, every workgroup taking a fixed
+// share of the rows.  Each workgroup writes one fp32 partial row of dgamma.
+// (A grid that does not divide evenly over the CUs leaves a tail: 819
+// workgroups for N = 5120 ran 20 % slower than 512.)
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kBwdResidentWaves = 16;
 // Upper bound on the backward grid, hence on the partial rows a workspace
 // must hold (rmsnorm_bwd_workspace_bytes promises this many rows at most).
 constexpr int64_t kBwdGridMax = 1024;
 // The forward grid is not persistent; it is only capped so that the grid
 // dimension stays small (rows beyond it are taken in further steps).
 constexpr int64_t kFwdGridMax = 1 << 20;
-constexpr int kFwdBlockWaves = 4;   // 256-thread forward workgroups (several row groups)
-constexpr int kBwdBlockWaves = 16;  // 1024-thread backward workgroups
 // Register budget per lane for the row data, in 32-bit registers (of the 128
 // a lane of a 1024-thread workgroup may use): the forward holds x and gamma
-// packed, the backward holds x and dy packed plus one fp32 dgamma partial
-// per column it owns.
+// packed; the backward holds x and dy packed plus, per column it owns, the
+// fp32 weight and dgamma partial.
 constexpr int kLaneDataRegs = 96;
 
 int elsize(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
@@ -53,7 +64,7 @@ int64_t matrix_bytes(int64_t M, int64_t N, int64_t stride, int dtype) {
 int check_common(int64_t M, int64_t N, int64_t stride, int dtype, int gemma) {
   if (dtype != RMSNORM_F32 && dtype != RMSNORM_BF16) return RMSNORM_E_DTYPE;
   if (gemma != 0 && gemma != 1) return RMSNORM_E_FLAG;
-  if (M < 0 || N < 1 || N > RMSNORM_N_MAX) return RMSNORM_E_SHAPE;
+  if (M < 0 || M > RMSNORM_M_MAX || N < 1 || N > RMSNORM_N_MAX) return RMSNORM_E_SHAPE;
   if (stride < N) return RMSNORM_E_STRIDE;
   // element offsets must stay well inside int64 even for the last row
   if (M > 0 && stride > (std::numeric_limits<int64_t>::max() / 8) / M) return RMSNORM_E_SHAPE;
@@ -71,35 +82,33 @@ int choose_vec(int dtype, int64_t N, int64_t stride, std::initializer_list<const
   return 1;
 }
 
-// Waves per row and vectors per lane: among 1..16 waves per row, the shape
-// whose compiled register-array length wastes the fewest lanes (ties go to
-// fewer waves, which need fewer barriers).
+// Waves per row and vectors per lane: among 1..16 waves per row and the
+// compiled register-array lengths, the shape that wastes the fewest lanes;
+// ties go to the length nearest kLaneVectors, then to fewer waves.
 bool row_shape(int64_t nvec, int iters_cap, int* wpr, int* iters) {
-  int64_t best = -1;
+  int64_t best_waste = -1;
+  int best_dist = 0;
   for (int w = 1; w <= kMaxBlockWaves; ++w) {
-    const int64_t need = ceil_div(nvec, int64_t(kWave) * w);
-    int it = -1;
-    for (int v : kItersSet)
-      if (v >= need) {
-        it = v;
-        break;
+    for (int it : kItersSet) {
+      if (it > iters_cap || int64_t(it) * kWave * w < nvec) continue;
+      const int64_t waste = int64_t(it) * kWave * w - nvec;
+      const int dist = it > kLaneVectors ? it - kLaneVectors : kLaneVectors - it;
+      if (best_waste < 0 || waste < best_waste || (waste == best_waste && dist < best_dist)) {
+        best_waste = waste;
+        best_dist = dist;
+        *wpr = w;
+        *iters = it;
       }
-    if (it < 0 || it > iters_cap) continue;
-    const int64_t waste = int64_t(it) * kWave * w - nvec;
-    if (best < 0 || waste < best) {
-      best = waste;
-      *wpr = w;
-      *iters = it;
     }
   }
-  return best >= 0;
+  return best_waste >= 0;
 }
 
 // Elements per lane the register budget allows.
 int lane_elems_cap(int dtype, bool backward) {
   const int es = elsize(dtype);
-  // registers per element: packed operands (es/4 each), plus 1 for the fp32 partial
-  return backward ? kLaneDataRegs * 4 / (2 * es + 4) : kLaneDataRegs * 4 / (2 * es);
+  // registers per element, in quarters: packed operands (es each), fp32 values (4 each)
+  return backward ? kLaneDataRegs * 4 / (2 * es + 8) : kLaneDataRegs * 4 / (2 * es);
 }
 
 RowPlan plan_rows(int64_t M, int64_t N, int vec, int dtype, bool backward) {
@@ -111,10 +120,12 @@ RowPlan plan_rows(int64_t M, int64_t N, int vec, int dtype, bool backward) {
     p.iters = 0;  // cannot happen for N <= RMSNORM_N_MAX
     return p;
   }
-  const int block_waves = backward ? kBwdBlockWaves : kFwdBlockWaves;
-  p.rpb = std::max(1, block_waves / p.wpr);
+  p.rpb = std::max(1, kBlockWaves / p.wpr);
   const int64_t groups = ceil_div(M, p.rpb);
-  p.grid = std::max<int64_t>(1, std::min(groups, backward ? kBwdGrid : kFwdGridMax));
+  int64_t per_cu = 1;
+  while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
+  const int64_t grid_cap = backward ? std::min(kBwdGridMax, kComputeUnits * per_cu) : kFwdGridMax;
+  p.grid = std::max<int64_t>(1, std::min(groups, grid_cap));
   p.row_iters = ceil_div(groups, p.grid);
   return p;
 }
@@ -254,7 +265,7 @@ int rmsnorm_bwd_rows(const void* x, const void* gamma, const void* dy, const flo
 }
 
 int rmsnorm_dgamma_reduce(const float* partials, int64_t rows, int64_t N, float* dgamma, hipStream_t stream) {
-  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX) return RMSNORM_E_SHAPE;
+  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX || rows * N > RMSNORM_PARTIALS_MAX) return RMSNORM_E_SHAPE;
   if (!dgamma || (rows > 0 && !partials)) return RMSNORM_E_NULL;
   if (!aligned(dgamma, 4) || (rows > 0 && !aligned(partials, 4))) return RMSNORM_E_ALIGN;
   if (rows > 0 && overlap(span(partials, rows * N * 4), span(dgamma, N * 4))) return RMSNORM_E_ALIAS;

@@ -11,9 +11,16 @@
 // (about 1 flop per byte), so there is no MFMA: everything is about moving
 // each byte of x, dy, y and dx through HBM exactly once.
 //  - Each lane owns whole 16-byte column vectors of a row (8 bf16 or 4 fp32)
-//    and issues all of its loads for the row before any arithmetic, so a
-//    wave has the whole row (or its share of it) in flight at once; a row is
+//    and issues all of its loads for the row before any arithmetic; a row is
 //    read once and never re-read.
+//  - Every row access is a raw buffer load/store through a per-row buffer
+//    descriptor whose range is the row's bytes (zero for rows past M).  The
+//    hardware range check turns the masked tail and missing rows into
+//    zero-returning loads and dropped stores, so every access is one
+//    unconditional instruction: no branches around memory operations, and
+//    the compiler can count the operations in flight exactly (with
+//    branch-guarded loads it has to wait for all of them, which serialises
+//    the backward's row pipeline).
 //  - Upcast to fp32 on load; sums in fp32; one rounding (RNE, the gfx950
 //    packed bf16 convert) on store.
 //  - Row sums are reduced inside the wave with DPP row operations, a
@@ -22,11 +29,11 @@
 //    barrier; the LDS slots are double-buffered by step parity so one barrier
 //    per row suffices.
 //  - The backward is a persistent grid: each workgroup owns a fixed set of
-//    rows, keeps gamma and its dgamma column partials in registers across
-//    them, and writes one fp32 partial row at the end (row groups of the
-//    workgroup are combined in LDS in a fixed order).  A second small kernel
-//    sums the partial rows per column in a fixed order.  No atomics touch
-//    data, so every result is bitwise reproducible.
+//    rows, keeps the weight and its dgamma column partials in registers
+//    across them, and writes one fp32 partial row at the end (row groups of the workgroup
+//    are combined in LDS in a fixed order).  A second small kernel sums the
+//    partial rows per column in a fixed order.  No atomics touch data, so
+//    every result is bitwise reproducible.
 //  - dx may be written over dy: each lane reads its own dy elements before it
 //    writes the same elements of dx, and no other lane touches them.
 #include <hip/hip_runtime.h>
@@ -41,6 +48,22 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family:
+// 32-bit data format; the range check is then offset against the byte count.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy operand of buffer instructions: 0 = default, 2 = nontemporal.
+constexpr int kDefault = 0;
+constexpr int kNontemporal = 2;
+
+// A descriptor for `bytes` bytes at `base`; accesses at or past `bytes` read
+// zero and write nothing.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
 
 // VEC consecutive elements with the storage type S (float, or uint16_t for
 // bf16 bits), aligned to their full width so one load/store moves them.  They
@@ -83,23 +106,68 @@ struct alignas(sizeof(S) * VEC) Pack {
   }
 };
 
-template <int VEC>
-__device__ __forceinline__ void store_f32(float* dst, const float (&o)[VEC]) {
-  Pack<float, VEC> p;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) p.w[e] = __builtin_bit_cast(uint32_t, o[e]);
-  *reinterpret_cast<Pack<float, VEC>*>(dst) = p;
+// One pack from a buffer at byte offset `off`.  The whole offset goes in the
+// instruction's vector offset, which the range check covers (the scalar
+// offset operand is left at zero: it is added to the address but not checked).
+template <typename S, int VEC, int AUX>
+__device__ __forceinline__ Pack<S, VEC> buf_load(Rsrc r, uint32_t off) {
+  typedef Pack<S, VEC> P;
+  if constexpr (P::kBytes == 16) {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+  } else if constexpr (P::kBytes == 8) {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+  } else if constexpr (P::kBytes == 4) {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
+  } else {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX));
+  }
 }
 
-// Round VEC fp32 values once (to nearest even) to the storage type and store.
-template <int VEC>
-__device__ __forceinline__ void store_out(float* dst, const float (&o)[VEC]) {
-  store_f32<VEC>(dst, o);
+template <typename S, int VEC, int AUX>
+__device__ __forceinline__ void buf_store(const Pack<S, VEC>& p, Rsrc r, uint32_t off) {
+  typedef Pack<S, VEC> P;
+  if constexpr (P::kBytes == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, p), r, off, 0, AUX);
+  } else if constexpr (P::kBytes == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, p), r, off, 0, AUX);
+  } else if constexpr (P::kBytes == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p), r, off, 0, AUX);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, p), r, off, 0, AUX);
+  }
 }
-template <int VEC>
-__device__ __forceinline__ void store_out(uint16_t* dst, const float (&o)[VEC]) {
-  Pack<uint16_t, VEC> p;
-  if constexpr (VEC == 1) {
+
+// VEC fp32 values at byte offset `off`, in stores of at most 16 bytes.
+template <int VEC, int AUX>
+__device__ __forceinline__ void buf_store_f32(const float (&v)[VEC], Rsrc r, uint32_t off) {
+  if constexpr (VEC > 4) {
+#pragma unroll
+    for (int k = 0; k < VEC; k += 4) {
+      const u32x4_t q = {__builtin_bit_cast(uint32_t, v[k]), __builtin_bit_cast(uint32_t, v[k + 1]),
+                         __builtin_bit_cast(uint32_t, v[k + 2]), __builtin_bit_cast(uint32_t, v[k + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(q, r, off + k * 4u, 0, AUX);
+    }
+  } else {
+    Pack<float, VEC> p;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p.w[e] = __builtin_bit_cast(uint32_t, v[e]);
+    buf_store<float, VEC, AUX>(p, r, off);
+  }
+}
+
+// Byte offset that is out of range of every descriptor made here (their
+// ranges are below 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+// Round VEC fp32 values once (to nearest even; gfx950 converts bf16 pairs in
+// one instruction) to the storage type S.
+template <typename S, int VEC>
+__device__ __forceinline__ Pack<S, VEC> round_pack(const float (&o)[VEC]) {
+  Pack<S, VEC> p;
+  if constexpr (sizeof(S) == 4) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p.w[e] = __builtin_bit_cast(uint32_t, o[e]);
+  } else if constexpr (VEC == 1) {
     p.w[0] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[0]));
   } else {
 #pragma unroll
@@ -108,19 +176,6 @@ __device__ __forceinline__ void store_out(uint16_t* dst, const float (&o)[VEC]) 
       p.w[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
     }
   }
-  *reinterpret_cast<Pack<uint16_t, VEC>*>(dst) = p;
-}
-
-template <typename S, int VEC>
-__device__ __forceinline__ Pack<S, VEC> load_pack(const S* src) {
-  return *reinterpret_cast<const Pack<S, VEC>*>(src);
-}
-
-template <typename S, int VEC>
-__device__ __forceinline__ Pack<S, VEC> zero_pack() {
-  Pack<S, VEC> p;
-#pragma unroll
-  for (int k = 0; k < Pack<S, VEC>::kWords; ++k) p.w[k] = 0;
   return p;
 }
 
@@ -158,6 +213,39 @@ __device__ __forceinline__ float group_sum(float wave_total, float (*red)[kMaxBl
   return t;
 }
 
+// Where a lane sits: its wave (uniform, in a scalar register), the row group
+// of the wave and the wave within the group.
+struct Lane {
+  int lane, wave, group, wv;
+  __device__ __forceinline__ explicit Lane(int wpr) {
+    lane = threadIdx.x & (kWave - 1);
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    group = wave / wpr;
+    wv = wave - group * wpr;
+  }
+  // index of the lane's first column vector in a row
+  __device__ __forceinline__ uint32_t first_vec() const { return static_cast<uint32_t>(wv * kWave + lane); }
+};
+
+// Row handled by row group `group` of this workgroup at step `step`.
+__device__ __forceinline__ int64_t row_of(int64_t step, int rpb, int group) {
+  return (step * gridDim.x + blockIdx.x) * rpb + group;
+}
+
+// ---------------------------------------------------------------------------
+// Cache policy of the streamed row operands: every byte of x, dy, y and dx is
+// touched once per pass, so all of them use the nontemporal forms, which do
+// not allocate in L2 or the 256 MB Infinity Cache.  Measured on MI355X at
+// 16384 x 8192 bf16: an allocating x load in the forward loses a third of
+// the forward's bandwidth when the cache holds dirty lines (each allocation
+// then costs a write-back), and only pays off when the backward of the same
+// rows runs right after the forward and finds x still cached.
+// ---------------------------------------------------------------------------
+constexpr int kFwdLoadX = kNontemporal;
+constexpr int kFwdStoreY = kNontemporal;
+constexpr int kBwdLoadXdy = kNontemporal;
+constexpr int kBwdStoreDx = kNontemporal;
+
 // ---------------------------------------------------------------------------
 // Forward: y = x * r * w, rstd = r.
 // One step per row group: the grid covers the rows (capped, then looped), so
@@ -166,35 +254,32 @@ __device__ __forceinline__ float group_sum(float wave_total, float (*red)[kMaxBl
 // ---------------------------------------------------------------------------
 template <typename S, int VEC, int ITERS>
 __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int group = wave / a.wpr;
-  const int wv = wave - group * a.wpr;
+  constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  const Lane L(a.wpr);
   __shared__ float red[2][kMaxBlockWaves];
 
-  const S* __restrict__ x = static_cast<const S*>(a.x);
-  const S* __restrict__ gamma = static_cast<const S*>(a.gamma);
-  S* __restrict__ y = static_cast<S*>(a.y);
+  const uint32_t voff = L.first_vec() * kPack;
+  const uint32_t iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  const Rsrc rg = make_rsrc(a.gamma, row_bytes);
+  const Rsrc rr = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+  const S* x = static_cast<const S*>(a.x);
+  S* y = static_cast<S*>(a.y);
 
   for (int64_t step = 0; step < a.row_iters; ++step) {
-    const int64_t row = (step * gridDim.x + blockIdx.x) * a.rpb + group;
+    const int64_t row = row_of(step, a.rpb, L.group);
     const bool active = row < a.M;
     const int64_t off = active ? row * a.stride : 0;
+    const Rsrc rx = make_rsrc(x + off, active ? row_bytes : 0u);
+    const Rsrc ry = make_rsrc(y + off, active ? row_bytes : 0u);
 
     // all of this lane's loads for the row first: x, then gamma
     Pack<S, VEC> xv[ITERS];
     Pack<S, VEC> gv[ITERS];
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      xv[i] = (active && v < a.nvec) ? load_pack<S, VEC>(x + off + static_cast<int64_t>(v) * VEC) : zero_pack<S, VEC>();
-    }
+    for (int i = 0; i < ITERS; ++i) xv[i] = buf_load<S, VEC, kFwdLoadX>(rx, voff + i * iter_bytes);
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      gv[i] = (active && v < a.nvec) ? load_pack<S, VEC>(gamma + v * VEC) : zero_pack<S, VEC>();
-    }
+    for (int i = 0; i < ITERS; ++i) gv[i] = buf_load<S, VEC, kDefault>(rg, voff + i * iter_bytes);
 
     float ss = 0.f;
 #pragma unroll
@@ -207,131 +292,160 @@ __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) xv[i].keep_packed();
     ss = wave_sum(ss);
-    if (a.wpr > 1) ss = group_sum(ss, red, step, wave, group, a.wpr, lane);
+    if (a.wpr > 1) ss = group_sum(ss, red, step, L.wave, L.group, a.wpr, L.lane);
 
     // mean over the true N (not a padded width), eps under the root
     const float r = rsqrtf(fmaf(ss, a.inv_n, a.eps));
-    if (active && wv == 0 && lane == 0) a.rstd[row] = r;
+    // one lane per row writes r; every other lane's offset is out of range
+    const bool writer = active && L.wv == 0 && L.lane == 0;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r), rr,
+                                          writer ? static_cast<uint32_t>(row) * 4u : kOutOfRange, 0, kDefault);
 
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      if (active && v < a.nvec) {
-        float o[VEC];
+      float o[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = (xv[i].get(e) * r) * (gv[i].get(e) + a.w_off);
-        store_out<VEC>(y + off + static_cast<int64_t>(v) * VEC, o);
-      }
+      for (int e = 0; e < VEC; ++e) o[e] = (xv[i].get(e) * r) * (gv[i].get(e) + a.w_off);
+      buf_store<S, VEC, kFwdStoreY>(round_pack<S, VEC>(o), ry, voff + i * iter_bytes);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Backward row pass: dx, and per-workgroup dgamma partial rows.
-// Persistent: each workgroup takes a fixed set of rows.  The weight
-// w = gamma (+1 for Gemma) is converted to fp32 once per workgroup into LDS;
-// the dgamma partials of a lane's columns live in registers across all its
-// rows.
+// Persistent: each workgroup takes a fixed set of rows.  A lane keeps, for
+// the columns it owns, the weight w = gamma (+1 for Gemma) in fp32 and its
+// dgamma partials in fp32 registers across all its rows.
 // ---------------------------------------------------------------------------
 template <typename S, int VEC, int ITERS>
-__global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float lds_w[];  // N floats: w, later reused to combine the partial rows
-  __shared__ float red[2][kMaxBlockWaves];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int group = wave / a.wpr;
-  const int wv = wave - group * a.wpr;
+struct BwdRow {
+  Pack<S, VEC> x[ITERS];
+  Pack<S, VEC> dy[ITERS];
+  float r;
+};
 
-  const S* __restrict__ x = static_cast<const S*>(a.x);
-  const S* __restrict__ gamma = static_cast<const S*>(a.gamma);
-  const float* __restrict__ rstd = a.rstd;
-  // dy and dx may be the same buffer: no __restrict__ on either.
-  const S* dy = static_cast<const S*>(a.dy);
-  S* dx = static_cast<S*>(a.dx);
+// Offsets and descriptors a backward lane uses for every row.
+struct BwdGeom {
+  uint32_t voff;        // byte offset of the lane's first vector in a row
+  uint32_t iter_bytes;  // bytes between the lane's successive vectors
+  uint32_t row_bytes;   // N * sizeof(S)
+  Rsrc rstd;            // the M saved r values
+};
 
-  for (int c = tid; c < a.N; c += blockDim.x) {
-    const Pack<S, 1> g = load_pack<S, 1>(gamma + c);
-    lds_w[c] = g.get(0) + a.w_off;
+template <typename S, int VEC, int ITERS>
+__device__ __forceinline__ void bwd_load_row(BwdRow<S, VEC, ITERS>& t, const BwdArgs& a, int64_t step, const Lane& L,
+                                             const BwdGeom& G) {
+  const int64_t row = row_of(step, a.rpb, L.group);
+  const bool active = row < a.M;
+  const int64_t off = active ? row * a.stride : 0;
+  const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? G.row_bytes : 0u);
+  const Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + off, active ? G.row_bytes : 0u);
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    t.x[i] = buf_load<S, VEC, kBwdLoadXdy>(rx, G.voff + i * G.iter_bytes);
+    t.dy[i] = buf_load<S, VEC, kBwdLoadXdy>(rd, G.voff + i * G.iter_bytes);
   }
-  __syncthreads();
+  // r of a missing row reads as zero (out of the descriptor's range)
+  t.r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                      G.rstd, active ? static_cast<uint32_t>(row) * 4u : kOutOfRange, 0, kDefault));
+}
 
-  float acc[ITERS][VEC];
+template <typename S, int VEC, int ITERS>
+__device__ __forceinline__ void bwd_process_row(BwdRow<S, VEC, ITERS>& t, const BwdArgs& a, int64_t step,
+                                                const float (&w)[ITERS][VEC], float (&acc)[ITERS][VEC],
+                                                float (*red)[kMaxBlockWaves], const Lane& L, const BwdGeom& G) {
+  const int64_t row = row_of(step, a.rpb, L.group);
+  const bool active = row < a.M;
+  const int64_t off = active ? row * a.stride : 0;
+  // dx may be the dy buffer itself; every element of dy this lane owns was
+  // loaded into registers before this point
+  const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + off, active ? G.row_bytes : 0u);
+
+  // sum over the row of u*x with u = dy*w
+  float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < ITERS; ++i)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[i][e] = 0.f;
-
-  for (int64_t step = 0; step < a.row_iters; ++step) {
-    const int64_t row = (step * gridDim.x + blockIdx.x) * a.rpb + group;
-    const bool active = row < a.M;
-    const int64_t off = active ? row * a.stride : 0;
-
-    Pack<S, VEC> xv[ITERS];
-    Pack<S, VEC> dv[ITERS];
+    for (int e = 0; e < VEC; ++e) dot = fmaf(t.dy[i].get(e) * w[i][e], t.x[i].get(e), dot);
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      const bool ok = active && v < a.nvec;
-      xv[i] = ok ? load_pack<S, VEC>(x + off + static_cast<int64_t>(v) * VEC) : zero_pack<S, VEC>();
-      dv[i] = ok ? load_pack<S, VEC>(dy + off + static_cast<int64_t>(v) * VEC) : zero_pack<S, VEC>();
+  for (int i = 0; i < ITERS; ++i) {
+    t.x[i].keep_packed();
+    t.dy[i].keep_packed();
+  }
+  dot = wave_sum(dot);
+  if (a.wpr > 1) dot = group_sum(dot, red, step, L.wave, L.group, a.wpr, L.lane);
+
+  // dx = r*u - x * (r^3 * mean(u*x)), mean over the true N
+  const float r = t.r;
+  const float c = r * r * r * (dot * a.inv_n);
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float xf = t.x[i].get(e);
+      const float df = t.dy[i].get(e);
+      o[e] = fmaf(-xf, c, r * (df * w[i][e]));
+      acc[i][e] = fmaf(df * xf, r, acc[i][e]);  // dgamma contribution dy*x*r (zero past the row's end)
     }
-    const float r = active ? rstd[row] : 0.f;
+    buf_store<S, VEC, kBwdStoreDx>(round_pack<S, VEC>(o), rdx, G.voff + i * G.iter_bytes);
+  }
+}
 
-    // sum over the row of u*x with u = dy*w
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      const Pack<float, VEC> w = load_pack<float, VEC>(lds_w + (v < a.nvec ? v : 0) * VEC);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) dot = fmaf(dv[i].get(e) * w.get(e), xv[i].get(e), dot);
-    }
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      xv[i].keep_packed();
-      dv[i].keep_packed();
-    }
-    dot = wave_sum(dot);
-    if (a.wpr > 1) dot = group_sum(dot, red, step, wave, group, a.wpr, lane);
+template <typename S, int VEC, int ITERS>
+__global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float comb[];  // N floats, when rpb > 1
+  __shared__ float red[2][kMaxBlockWaves];
+  constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  const Lane L(a.wpr);
+  BwdGeom G;
+  G.voff = L.first_vec() * kPack;
+  G.iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
+  G.row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  G.rstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
 
-    // dx = r*u - x * (r^3 * mean(u*x)), mean over the true N
-    const float c = r * r * r * (dot * a.inv_n);
+  BwdRow<S, VEC, ITERS> ta;
+
+  float w[ITERS][VEC];
+  float acc[ITERS][VEC];
+  {
+    const Rsrc rg = make_rsrc(a.gamma, G.row_bytes);
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      if (active && v < a.nvec) {
-        const Pack<float, VEC> w = load_pack<float, VEC>(lds_w + v * VEC);
-        float o[VEC];
+      const Pack<S, VEC> g = buf_load<S, VEC, kDefault>(rg, G.voff + i * G.iter_bytes);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float xf = xv[i].get(e);
-          const float df = dv[i].get(e);
-          o[e] = fmaf(-xf, c, r * (df * w.get(e)));
-          acc[i][e] = fmaf(df * xf, r, acc[i][e]);  // dgamma contribution dy*x*r
-        }
-        store_out<VEC>(dx + off + static_cast<int64_t>(v) * VEC, o);
+      for (int e = 0; e < VEC; ++e) {
+        w[i][e] = g.get(e) + a.w_off;
+        acc[i][e] = 0.f;
       }
     }
+  }
+
+  // One row at a time.  (Measured on MI355X at 16384 x 8192 bf16: keeping a
+  // second row's loads in flight during a row's work, in 88 instead of ~64
+  // registers, made this pass about 6 % slower; the other waves on the CU
+  // already cover a row's reduction and barrier.)
+  for (int64_t step = 0; step < a.row_iters; ++step) {
+    bwd_load_row(ta, a, step, L, G);
+    bwd_process_row(ta, a, step, w, acc, red, L, G);
   }
 
   // One partial row per workgroup: row groups are added in LDS in group order.
   float* prow = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
   if (a.rpb == 1) {
+    const Rsrc rp = make_rsrc(prow, static_cast<uint32_t>(a.N) * 4u);
+    const uint32_t voff32 = L.first_vec() * VEC * 4u;
+    const uint32_t iter32 = static_cast<uint32_t>(a.wpr) * kWave * VEC * 4u;
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int v = (i * a.wpr + wv) * kWave + lane;
-      if (v < a.nvec) store_f32<VEC>(prow + v * VEC, acc[i]);
-    }
+    for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kDefault>(acc[i], rp, voff32 + i * iter32);
     return;
   }
-  float* comb = lds_w;  // w is no longer needed once every wave passes the next barrier
   for (int g = 0; g < a.rpb; ++g) {
     __syncthreads();
-    if (group == g) {
+    if (L.group == g) {
 #pragma unroll
       for (int i = 0; i < ITERS; ++i) {
-        const int v = (i * a.wpr + wv) * kWave + lane;
+        const int v = (i * a.wpr + L.wv) * kWave + L.lane;
         if (v < a.nvec) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
@@ -343,33 +457,39 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
     }
   }
   __syncthreads();
-  for (int col = tid; col < a.N; col += blockDim.x) prow[col] = comb[col];
+  for (int col = threadIdx.x; col < a.N; col += blockDim.x) prow[col] = comb[col];
 }
-
 
 // ---------------------------------------------------------------------------
 // dgamma[j] = sum over partial rows p (in order) of partials[p, j].
 // Block: kReduceCols column threads (VEC columns each) x kReduceSlices row
 // slices; slice s sums rows s, s + slices, ...; the slices are then added in
-// slice order.
+// slice order.  Loads go through a descriptor over the whole partials table,
+// so rows past the end read as zero and every load is unconditional.
 // ---------------------------------------------------------------------------
 template <int VEC>
 __global__ __launch_bounds__(kReduceCols * kReduceSlices) void rmsnorm_dgamma_reduce_kernel(const ReduceArgs a) {
+  constexpr int kUnroll = 16;
   __shared__ float part[kReduceSlices][kReduceCols * VEC];
   const int tc = threadIdx.x % kReduceCols;
   const int ts = threadIdx.x / kReduceCols;
   const int col = (blockIdx.x * kReduceCols + tc) * VEC;
+  const Rsrc rp = make_rsrc(a.partials, static_cast<uint32_t>(a.rows * a.N) * 4u);
+  const uint32_t slice_bytes = static_cast<uint32_t>(kReduceSlices) * static_cast<uint32_t>(a.N) * 4u;
+  const uint32_t voff = (static_cast<uint32_t>(ts) * static_cast<uint32_t>(a.N) + static_cast<uint32_t>(col)) * 4u;
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  if (col < a.N) {
-    const float* __restrict__ p = a.partials + col;
-#pragma unroll 8
-    for (int64_t row = ts; row < a.rows; row += kReduceSlices) {
-      const Pack<float, VEC> v = load_pack<float, VEC>(p + row * a.N);
+  const int64_t trips = (a.rows + kReduceSlices - 1) / kReduceSlices;
+  for (int64_t k = 0; k < trips; k += kUnroll) {
+    Pack<float, VEC> v[kUnroll];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += v.get(e);
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = buf_load<float, VEC, kDefault>(rp, voff + static_cast<uint32_t>(k + u) * slice_bytes);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += v[u].get(e);
   }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) part[ts][tc * VEC + e] = acc[e];
@@ -382,7 +502,7 @@ __global__ __launch_bounds__(kReduceCols * kReduceSlices) void rmsnorm_dgamma_re
       for (int s = 1; s < kReduceSlices; ++s) t += part[s][tc * VEC + e];
       o[e] = t;
     }
-    store_f32<VEC>(a.dgamma + col, o);
+    *reinterpret_cast<Pack<float, VEC>*>(a.dgamma + col) = round_pack<float, VEC>(o);
   }
 }
 
@@ -398,13 +518,13 @@ hipError_t fwd_inst(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
 
 template <typename S, int VEC, int ITERS>
 hipError_t bwd_inst(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(a.N) * sizeof(float);
+  const size_t lds = p.rpb > 1 ? static_cast<size_t>(a.N) * sizeof(float) : 0;
   hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)),
                      dim3(p.threads()), lds, s, a);
   return hipGetLastError();
 }
 
-template <typename S, int VEC, typename Args, hipError_t (*L1)(const RowPlan&, const Args&, hipStream_t),
+template <typename Args, hipError_t (*L1)(const RowPlan&, const Args&, hipStream_t),
           hipError_t (*L2)(const RowPlan&, const Args&, hipStream_t), hipError_t (*L4)(const RowPlan&, const Args&, hipStream_t),
           hipError_t (*L5)(const RowPlan&, const Args&, hipStream_t), hipError_t (*L8)(const RowPlan&, const Args&, hipStream_t),
           hipError_t (*L16)(const RowPlan&, const Args&, hipStream_t)>
@@ -422,13 +542,13 @@ hipError_t pick_iters(const RowPlan& p, const Args& a, hipStream_t s) {
 
 template <typename S, int VEC>
 hipError_t fwd_vec(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
-  return pick_iters<S, VEC, FwdArgs, fwd_inst<S, VEC, 1>, fwd_inst<S, VEC, 2>, fwd_inst<S, VEC, 4>, fwd_inst<S, VEC, 5>,
+  return pick_iters<FwdArgs, fwd_inst<S, VEC, 1>, fwd_inst<S, VEC, 2>, fwd_inst<S, VEC, 4>, fwd_inst<S, VEC, 5>,
                     fwd_inst<S, VEC, 8>, fwd_inst<S, VEC, 16>>(p, a, s);
 }
 
 template <typename S, int VEC>
 hipError_t bwd_vec(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-  return pick_iters<S, VEC, BwdArgs, bwd_inst<S, VEC, 1>, bwd_inst<S, VEC, 2>, bwd_inst<S, VEC, 4>, bwd_inst<S, VEC, 5>,
+  return pick_iters<BwdArgs, bwd_inst<S, VEC, 1>, bwd_inst<S, VEC, 2>, bwd_inst<S, VEC, 4>, bwd_inst<S, VEC, 5>,
                     bwd_inst<S, VEC, 8>, bwd_inst<S, VEC, 16>>(p, a, s);
 }
 
