@@ -227,8 +227,11 @@ struct Lane {
   __device__ __forceinline__ uint32_t first_vec() const { return static_cast<uint32_t>(wv * kWave + lane); }
 };
 
-// Row handled by row group `group` of this workgroup at step `step`.
-__device__ __forceinline__ int64_t row_of(int64_t step, int rpb, int group) {
+// Row handled by row group `group` of this workgroup at step `step` (of
+// `row_iters`): at each step the workgroups cover consecutive rows, so the
+// rows in flight across the chip form one compact window.
+__device__ __forceinline__ int64_t row_of(int64_t step, int64_t row_iters, int rpb, int group) {
+  (void)row_iters;
   return (step * gridDim.x + blockIdx.x) * rpb + group;
 }
 
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
   S* y = static_cast<S*>(a.y);
 
   for (int64_t step = 0; step < a.row_iters; ++step) {
-    const int64_t row = row_of(step, a.rpb, L.group);
+    const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
     const bool active = row < a.M;
     const int64_t off = active ? row * a.stride : 0;
     const Rsrc rx = make_rsrc(x + off, active ? row_bytes : 0u);
@@ -335,7 +338,7 @@ struct BwdGeom {
 template <typename S, int VEC, int ITERS>
 __device__ __forceinline__ void bwd_load_row(BwdRow<S, VEC, ITERS>& t, const BwdArgs& a, int64_t step, const Lane& L,
                                              const BwdGeom& G) {
-  const int64_t row = row_of(step, a.rpb, L.group);
+  const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
   const bool active = row < a.M;
   const int64_t off = active ? row * a.stride : 0;
   const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? G.row_bytes : 0u);
@@ -354,7 +357,7 @@ template <typename S, int VEC, int ITERS>
 __device__ __forceinline__ void bwd_process_row(BwdRow<S, VEC, ITERS>& t, const BwdArgs& a, int64_t step,
                                                 const float (&w)[ITERS][VEC], float (&acc)[ITERS][VEC],
                                                 float (*red)[kMaxBlockWaves], const Lane& L, const BwdGeom& G) {
-  const int64_t row = row_of(step, a.rpb, L.group);
+  const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
   const bool active = row < a.M;
   const int64_t off = active ? row * a.stride : 0;
   // dx may be the dy buffer itself; every element of dy this lane owns was
