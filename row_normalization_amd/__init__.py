@@ -17,6 +17,7 @@ from ._lib import (
     rmsnorm_fwd,
     rmsnorm_status_string,
 )
+from .autograd import CALLS, RMSNorm, RMSNormFunction, rmsnorm
 
 __all__ = [
     "LIB_PATH",
@@ -29,4 +30,8 @@ __all__ = [
     "rmsnorm_dgamma_reduce",
     "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_status_string",
+    "rmsnorm",
+    "RMSNorm",
+    "RMSNormFunction",
+    "CALLS",
 ]

@@ -1,0 +1,91 @@
+"""PyTorch autograd adapter over the C ABI (training use).
+
+The adapter follows the shape the pages give for wiring the kernels into
+autograd: the Triton RMSNorm tutorial (partitech.com), section "Kết nối
+Autograd và thực sự huấn luyện" (a ``torch.autograd.Function`` whose forward
+saves x, gamma and the inverse RMS for the backward, whose backward returns
+one gradient per forward input, and a call counter that shows the kernel path
+was taken), and the Unsloth walkthrough's ``fast_rms_layernorm`` wrapper
+(section 3; the Gemma weight 1 + gamma).
+
+Every computation runs in the HIP kernels (``rmsnorm_fwd``, ``rmsnorm_bwd``);
+this module allocates outputs with torch and marshals arguments.  Inputs of
+any leading shape are flattened to rows of the last dimension, which must be
+contiguous.  The weight gradient is accumulated in fp32 by the library and
+cast to gamma's dtype here, because autograd requires a gradient of the
+parameter's own dtype (``rmsnorm_bwd`` gives the fp32 values directly).
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import rmsnorm_bwd, rmsnorm_bwd_workspace_bytes, rmsnorm_fwd
+
+# Passes through the adapter (not kernel launches): forward and backward.
+CALLS = {"forward": 0, "backward": 0}
+
+
+def _rows(t: torch.Tensor) -> torch.Tensor:
+    """[..., N] -> [M, N] view with contiguous rows (a copy only if the last dim is strided)."""
+    if t.dim() == 0:
+        raise ValueError("RMSNorm needs at least one dimension")
+    t2 = t.reshape(-1, t.shape[-1])
+    if t2.shape[1] > 1 and t2.stride(1) != 1:
+        t2 = t2.contiguous()
+    return t2
+
+
+class RMSNormFunction(torch.autograd.Function):
+    """y = x * r * w with r = 1/sqrt(mean(x^2) + eps), w = gamma or 1 + gamma."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False):
+        x2 = _rows(x)
+        y = torch.empty(x2.shape, dtype=x.dtype, device=x.device)
+        rstd = torch.empty(x2.shape[0], dtype=torch.float32, device=x.device)
+        rmsnorm_fwd(x2, gamma, y, rstd, eps=eps, gemma=gemma)
+        ctx.save_for_backward(x2, gamma, rstd)
+        ctx.gemma = bool(gemma)
+        ctx.x_shape = x.shape
+        CALLS["forward"] += 1
+        return y.view(x.shape)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, gamma, rstd = ctx.saved_tensors
+        M, N = x2.shape
+        # the C ABI takes one row stride for x, dy and dx: use dense rows
+        # (dy.contiguous() as on the tutorial; x only needs a copy if the
+        # caller's x was a strided view)
+        dy2 = dy.reshape(M, N).contiguous()
+        if M > 1 and x2.stride(0) != N:
+            x2 = x2.contiguous()
+        dx = torch.empty_like(dy2)
+        dgamma = torch.empty(N, dtype=torch.float32, device=dy.device)
+        ws_bytes = rmsnorm_bwd_workspace_bytes(M, N, x2.dtype)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dy.device)
+        rmsnorm_bwd(x2, gamma, dy2, rstd, dx, dgamma, ws, gemma=ctx.gemma)
+        CALLS["backward"] += 1
+        return dx.view(ctx.x_shape), dgamma.to(gamma.dtype), None, None
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False) -> torch.Tensor:
+    """Functional form: RMSNorm over the last dimension of x."""
+    return RMSNormFunction.apply(x, gamma, eps, gemma)
+
+
+class RMSNorm(torch.nn.Module):
+    """RMSNorm layer over the last dimension (weight initialised to 1, or 0 for Gemma's 1 + gamma)."""
+
+    def __init__(self, hidden: int, eps: float = 1e-6, gemma: bool = False, dtype=torch.bfloat16, device=None):
+        super().__init__()
+        init = torch.zeros if gemma else torch.ones
+        self.weight = torch.nn.Parameter(init(hidden, dtype=dtype, device=device))
+        self.eps = eps
+        self.gemma = gemma
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return rmsnorm(x, self.weight, self.eps, self.gemma)
+
+    def extra_repr(self) -> str:
+        return f"{self.weight.shape[0]}, eps={self.eps}, gemma={self.gemma}"

@@ -169,3 +169,12 @@ def test_python_binding_refuses_cpu_tensors():
         _lib._check(E_ALIAS, "probe")
     with pytest.raises(rn.RMSNormError):
         _lib._check(E_HIP, "probe")
+
+
+def test_autograd_adapter_refuses_cpu_tensors():
+    import torch
+
+    x = torch.randn(4, 8, requires_grad=True)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        rn.rmsnorm(x, torch.ones(8))
+    assert rn.RMSNorm(8, gemma=True).weight.detach().abs().sum() == 0
