@@ -22,10 +22,11 @@
  * Conventions for every entry point:
  *  - Matrices are row-major M x N with a row stride (in elements) shared by
  *    all matrices of one call; elements of a row are contiguous.
- *  - dtype is RMSNORM_F32 or RMSNORM_BF16 and applies to x, gamma, y, dy and
- *    dx.  rstd (the saved r) is always fp32[M]; dgamma and the partials are
- *    always fp32.  Arithmetic is fp32 in registers; each bf16 output is
- *    rounded once, to nearest even.
+ *  - dtype is RMSNORM_F32, RMSNORM_BF16 or RMSNORM_F16 and applies to x,
+ *    gamma, y, dy and dx.  rstd (the saved r) is always fp32[M]; dgamma and
+ *    the partials are always fp32.  Arithmetic is fp32 in registers; each
+ *    bf16/fp16 output is rounded to nearest even, once (twice for y with
+ *    RMSNORM_ROUND_NORMED).
  *  - All pointers are device pointers to memory the caller owns (for example
  *    PyTorch tensors).  The library allocates nothing and keeps no state
  *    between calls; calls are asynchronous on `stream` (0 = the null stream)
@@ -52,7 +53,19 @@
 extern "C" {
 #endif
 
-typedef enum { RMSNORM_F32 = 0, RMSNORM_BF16 = 1 } rmsnorm_dtype;
+typedef enum { RMSNORM_F32 = 0, RMSNORM_BF16 = 1, RMSNORM_F16 = 2 } rmsnorm_dtype;
+
+/* Bits of the `flags` argument.
+ *  RMSNORM_GEMMA         the weight is applied as (1 + gamma), formed in fp32
+ *                        (Unsloth walkthrough, section 3: the Gemma variant).
+ *  RMSNORM_ROUND_NORMED  forward only: round x*r to the I/O dtype before the
+ *                        weight multiply, y = T(T(x*r) * w), the order of the
+ *                        Hugging Face RMSNorm the walkthrough follows
+ *                        ("normed.to(W.dtype)" before "* W"); without it y is
+ *                        rounded once, y = T(x*r*w).  No effect for fp32.
+ *                        The backward accepts and ignores it (its formula
+ *                        treats the rounding as the identity). */
+enum { RMSNORM_GEMMA = 1, RMSNORM_ROUND_NORMED = 2 };
 
 typedef enum {
   RMSNORM_OK = 0,
@@ -61,11 +74,11 @@ typedef enum {
                                partials table (rows < 0 or rows * N > RMSNORM_PARTIALS_MAX) */
   RMSNORM_E_STRIDE = -3,    /* row_stride < N */
   RMSNORM_E_ALIGN = -4,     /* a pointer is not aligned to its element size */
-  RMSNORM_E_DTYPE = -5,     /* dtype is not RMSNORM_F32 / RMSNORM_BF16 */
+  RMSNORM_E_DTYPE = -5,     /* dtype is not RMSNORM_F32 / RMSNORM_BF16 / RMSNORM_F16 */
   RMSNORM_E_EPS = -6,       /* eps is not finite or not > 0 */
   RMSNORM_E_ALIAS = -7,     /* an output overlaps another buffer (dx == dy is the one allowed case) */
   RMSNORM_E_WORKSPACE = -8, /* workspace smaller than rmsnorm_bwd_workspace_bytes() */
-  RMSNORM_E_FLAG = -9,      /* gemma is not 0 or 1 */
+  RMSNORM_E_FLAG = -9,      /* flags has a bit other than RMSNORM_GEMMA | RMSNORM_ROUND_NORMED */
   RMSNORM_E_HIP = -10       /* a HIP launch failed */
 } rmsnorm_status;
 
@@ -87,11 +100,12 @@ typedef enum {
  *   rstd   [M] fp32, written: r_i, for rmsnorm_bwd_rows
  *   row_stride  elements between row starts of x and y (>= N)
  *   eps    finite, > 0; added to the mean of squares under the square root
- *   gemma  0: w = gamma;  1: w = 1 + gamma (formed in fp32)
+ *   flags  RMSNORM_GEMMA: w = 1 + gamma (formed in fp32), else w = gamma;
+ *          RMSNORM_ROUND_NORMED: the rounding order described above
  * M == 0 is a no-op.  y must not overlap x, gamma or rstd.
  */
 int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M, int64_t N,
-                int64_t row_stride, float eps, int dtype, int gemma, hipStream_t stream);
+                int64_t row_stride, float eps, int dtype, int flags, hipStream_t stream);
 
 /*
  * Size in bytes of the fp32 partials workspace rmsnorm_bwd_rows / rmsnorm_bwd
@@ -115,12 +129,12 @@ int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t* bytes);
  *   workspace  fp32, at least rmsnorm_bwd_workspace_bytes(); on return its
  *          first (*partial_rows) rows of N floats hold the partial sums
  *   partial_rows  out: number of partial rows written (0 when M == 0)
- *   gemma  as in rmsnorm_fwd
+ *   flags  as in rmsnorm_fwd (RMSNORM_GEMMA selects w = 1 + gamma)
  * dx must not overlap x, gamma, rstd or the workspace, except dx == dy.
  */
 int rmsnorm_bwd_rows(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx,
                      void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride,
-                     int dtype, int gemma, int64_t* partial_rows, hipStream_t stream);
+                     int dtype, int flags, int64_t* partial_rows, hipStream_t stream);
 
 /*
  * Second stage of the weight gradient: dgamma_j = sum over the `rows` partial
@@ -140,7 +154,7 @@ int rmsnorm_dgamma_reduce(const float* partials, int64_t rows, int64_t N, float*
  */
 int rmsnorm_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx, float* dgamma,
                 void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride, int dtype,
-                int gemma, hipStream_t stream);
+                int flags, hipStream_t stream);
 
 /* A static, human-readable description of a status code. */
 const char* rmsnorm_status_string(int status);

@@ -30,9 +30,14 @@ Readings of points the pages leave open:
   sum of dy*x*r as the plain variant.
 * The mean in r and in the dx projection divides by the true column count N.
 
+* The rounding order of [P1] ("normed.to(W.dtype)" before "* W", the
+  Hugging Face order) is ``forward_normed_rounded``: y = T(T(x*r) * w) with T
+  round-to-nearest-even to the I/O type, x*r taken exactly (fp64) before its
+  rounding.  ``forward`` is the single-rounding definition y = x*r*w.
+
 Every function here is pinned by ``tests/test_oracle.py`` (worked values
-printed on [P2], finite differences, closed-form identities, a library
-cross-check); none is "parity unpinned".
+printed on [P2], finite differences, closed-form identities, library
+cross-checks); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -95,3 +100,38 @@ def dgamma_from_rows(contributions) -> np.ndarray:
     rows directly, as the oracle of the second-stage reduction.
     """
     return np.sum(_f64(contributions), axis=0)
+
+
+# Significand bits (with the implicit one) of the 16-bit I/O types.
+_SIGNIFICAND_BITS = {"bf16": 8, "f16": 11}
+
+
+def quantize(v, dtype: str) -> np.ndarray:
+    """v rounded to nearest (ties to even) in the I/O type, returned as float64.
+
+    fp16 uses numpy's float16 conversion (correctly rounded, subnormals
+    included); bf16 keeps 8 significant bits of the fp64 value (frexp gives
+    m in [0.5, 1); m * 2^8 rounded half-to-even by ``np.round``).  bf16 has
+    fp32's exponent range, far from anything these values reach.
+    """
+    v = _f64(v)
+    if dtype == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return v.astype(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        m, e = np.frexp(v)
+        p = _SIGNIFICAND_BITS["bf16"]
+        return np.ldexp(np.round(m * 2.0**p), e - p)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def forward_normed_rounded(x, gamma, eps: float, gemma: bool, dtype: str):
+    """y = T(T(x * r) * w): the normalised row rounded to the I/O type before
+    the weight multiply, then the product rounded again [P1 §3].  Returns
+    (y [M,N], r [M])."""
+    x = _f64(x)
+    r = inverse_rms(x, eps)
+    normed = quantize(x * r[:, None], dtype)
+    w = weight(gamma, gemma)
+    return quantize(normed * w[None, :], dtype), r

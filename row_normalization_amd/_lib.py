@@ -18,8 +18,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librmsnorm.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "rmsnorm.h")
 
-F32, BF16 = 0, 1
-_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+F32, BF16, F16 = 0, 1, 2
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+GEMMA, ROUND_NORMED = 1, 2  # bits of the C ABI's flags argument
 
 STATUS = {
     0: "RMSNORM_OK", -1: "RMSNORM_E_NULL", -2: "RMSNORM_E_SHAPE", -3: "RMSNORM_E_STRIDE", -4: "RMSNORM_E_ALIGN",
@@ -87,7 +88,7 @@ def _check(status: int, what: str) -> None:
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPES:
-        raise ValueError(f"unsupported dtype {t.dtype}; the library takes float32 or bfloat16")
+        raise ValueError(f"unsupported dtype {t.dtype}; the library takes float32, bfloat16 or float16")
     return _DTYPES[t.dtype]
 
 
@@ -126,15 +127,23 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def rmsnorm_fwd(x, gamma, y, rstd, eps: float = 1e-6, gemma: bool = False, stream=None) -> None:
-    """y = x * r * w and rstd = r (w = gamma, or 1 + gamma with ``gemma``), on the GPU."""
+def _flags(gemma: bool, round_normed: bool = False) -> int:
+    return (GEMMA if gemma else 0) | (ROUND_NORMED if round_normed else 0)
+
+
+def rmsnorm_fwd(x, gamma, y, rstd, eps: float = 1e-6, gemma: bool = False, round_normed: bool = False,
+                stream=None) -> None:
+    """y = x * r * w and rstd = r (w = gamma, or 1 + gamma with ``gemma``), on the GPU.
+
+    ``round_normed`` rounds x * r to the I/O dtype before the weight multiply
+    (the Hugging Face order); by default y is rounded once."""
     _gpu(x, gamma, y, rstd)
     M, N, stride = _rows(x, "x")
     _same_layout(x, y, "y", stride)
     if rstd.dtype != torch.float32 or rstd.numel() != M or (M > 1 and rstd.stride(0) != 1):
         raise ValueError("rstd must be a contiguous float32 tensor of M elements")
     st = lib().rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, stride, float(eps), _dtype_code(x),
-                           int(bool(gemma)), _stream(stream))
+                           _flags(gemma, round_normed), _stream(stream))
     _check(st, "rmsnorm_fwd")
 
 
@@ -163,7 +172,7 @@ def rmsnorm_bwd_rows(x, gamma, dy, rstd, dx, workspace, gemma: bool = False, str
     rows = _c_i64(0)
     st = lib().rmsnorm_bwd_rows(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), M, N, stride, _dtype_code(x),
-                                int(bool(gemma)), ctypes.byref(rows), _stream(stream))
+                                _flags(gemma), ctypes.byref(rows), _stream(stream))
     _check(st, "rmsnorm_bwd_rows")
     return int(rows.value)
 
@@ -187,5 +196,5 @@ def rmsnorm_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, gemma: bool = False, 
         raise ValueError("dgamma must be float32 with N elements")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
-                           wbytes, M, N, stride, _dtype_code(x), int(bool(gemma)), _stream(stream))
+                           wbytes, M, N, stride, _dtype_code(x), _flags(gemma), _stream(stream))
     _check(st, "rmsnorm_bwd")

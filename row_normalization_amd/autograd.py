@@ -39,11 +39,12 @@ class RMSNormFunction(torch.autograd.Function):
     """y = x * r * w with r = 1/sqrt(mean(x^2) + eps), w = gamma or 1 + gamma."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False):
+    def forward(ctx, x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False,
+                round_normed: bool = False):
         x2 = _rows(x)
         y = torch.empty(x2.shape, dtype=x.dtype, device=x.device)
         rstd = torch.empty(x2.shape[0], dtype=torch.float32, device=x.device)
-        rmsnorm_fwd(x2, gamma, y, rstd, eps=eps, gemma=gemma)
+        rmsnorm_fwd(x2, gamma, y, rstd, eps=eps, gemma=gemma, round_normed=round_normed)
         ctx.save_for_backward(x2, gamma, rstd)
         ctx.gemma = bool(gemma)
         ctx.x_shape = x.shape
@@ -66,26 +67,33 @@ class RMSNormFunction(torch.autograd.Function):
         ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dy.device)
         rmsnorm_bwd(x2, gamma, dy2, rstd, dx, dgamma, ws, gemma=ctx.gemma)
         CALLS["backward"] += 1
-        return dx.view(ctx.x_shape), dgamma.to(gamma.dtype), None, None
+        return dx.view(ctx.x_shape), dgamma.to(gamma.dtype), None, None, None
 
 
-def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False) -> torch.Tensor:
-    """Functional form: RMSNorm over the last dimension of x."""
-    return RMSNormFunction.apply(x, gamma, eps, gemma)
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False,
+            round_normed: bool = False) -> torch.Tensor:
+    """Functional form: RMSNorm over the last dimension of x.
+
+    ``round_normed`` rounds x * r to x's dtype before the weight multiply (the
+    Hugging Face order); the gradient formula treats that rounding as the
+    identity."""
+    return RMSNormFunction.apply(x, gamma, eps, gemma, round_normed)
 
 
 class RMSNorm(torch.nn.Module):
     """RMSNorm layer over the last dimension (weight initialised to 1, or 0 for Gemma's 1 + gamma)."""
 
-    def __init__(self, hidden: int, eps: float = 1e-6, gemma: bool = False, dtype=torch.bfloat16, device=None):
+    def __init__(self, hidden: int, eps: float = 1e-6, gemma: bool = False, round_normed: bool = False,
+                 dtype=torch.bfloat16, device=None):
         super().__init__()
         init = torch.zeros if gemma else torch.ones
         self.weight = torch.nn.Parameter(init(hidden, dtype=dtype, device=device))
         self.eps = eps
         self.gemma = gemma
+        self.round_normed = round_normed
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return rmsnorm(x, self.weight, self.eps, self.gemma)
+        return rmsnorm(x, self.weight, self.eps, self.gemma, self.round_normed)
 
     def extra_repr(self) -> str:
         return f"{self.weight.shape[0]}, eps={self.eps}, gemma={self.gemma}"

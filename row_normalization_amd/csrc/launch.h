@@ -43,6 +43,7 @@ struct FwdArgs {
   int32_t wpr;
   int32_t rpb;
   int64_t row_iters;
+  int32_t round_normed;  // 1: round x*r to the I/O type before the weight multiply
 };
 
 struct BwdArgs {
@@ -79,7 +80,7 @@ constexpr int kItersMax = 16;
 constexpr int kReduceCols = 8;
 constexpr int kReduceSlices = 32;
 
-// dtype codes match rmsnorm_dtype.  Each returns hipSuccess or the launch error.
+// dtype codes match rmsnorm_dtype (0 fp32, 1 bf16, 2 fp16).  Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(int dtype, const RowPlan& p, const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStream_t s);
 hipError_t launch_dgamma_reduce(int vec, const ReduceArgs& a, hipStream_t s);

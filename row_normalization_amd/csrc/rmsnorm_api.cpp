@@ -62,9 +62,9 @@ int64_t matrix_bytes(int64_t M, int64_t N, int64_t stride, int dtype) {
   return M == 0 ? 0 : ((M - 1) * stride + N) * elsize(dtype);
 }
 
-int check_common(int64_t M, int64_t N, int64_t stride, int dtype, int gemma) {
-  if (dtype != RMSNORM_F32 && dtype != RMSNORM_BF16) return RMSNORM_E_DTYPE;
-  if (gemma != 0 && gemma != 1) return RMSNORM_E_FLAG;
+int check_common(int64_t M, int64_t N, int64_t stride, int dtype, int flags) {
+  if (dtype != RMSNORM_F32 && dtype != RMSNORM_BF16 && dtype != RMSNORM_F16) return RMSNORM_E_DTYPE;
+  if (flags & ~(RMSNORM_GEMMA | RMSNORM_ROUND_NORMED)) return RMSNORM_E_FLAG;
   if (M < 0 || M > RMSNORM_M_MAX || N < 1 || N > RMSNORM_N_MAX) return RMSNORM_E_SHAPE;
   if (stride < N) return RMSNORM_E_STRIDE;
   // element offsets must stay well inside int64 even for the last row
@@ -143,9 +143,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_E_H
 // Validation shared by rmsnorm_bwd_rows and rmsnorm_bwd.  `dgamma` is null
 // for the row pass alone.
 int check_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, const void* dx, const float* dgamma,
-              const void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t stride, int dtype, int gemma,
+              const void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t stride, int dtype, int flags,
               bool with_dgamma, int64_t* rows_written) {
-  int st = check_common(M, N, stride, dtype, gemma);
+  int st = check_common(M, N, stride, dtype, flags);
   if (st) return st;
   if (with_dgamma && !dgamma) return RMSNORM_E_NULL;
   if (with_dgamma && !aligned(dgamma, 4)) return RMSNORM_E_ALIGN;
@@ -174,7 +174,7 @@ int check_bwd(const void* x, const void* gamma, const void* dy, const float* rst
 }
 
 int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx,
-                            void* workspace, int64_t M, int64_t N, int64_t stride, int dtype, int gemma,
+                            void* workspace, int64_t M, int64_t N, int64_t stride, int dtype, int flags,
                             int64_t* rows_written, hipStream_t stream) {
   const int vec = choose_vec(dtype, N, stride, {x, gamma, dy, dx});
   const RowPlan p = plan_rows(M, N, vec, dtype, true);
@@ -191,7 +191,7 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
   a.N = static_cast<int32_t>(N);
   a.nvec = static_cast<int32_t>(N / vec);
   a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
-  a.w_off = gemma ? 1.0f : 0.0f;
+  a.w_off = (flags & RMSNORM_GEMMA) ? 1.0f : 0.0f;
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
@@ -214,8 +214,8 @@ using namespace rmsn;
 extern "C" {
 
 int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M, int64_t N, int64_t row_stride,
-                float eps, int dtype, int gemma, hipStream_t stream) {
-  int st = check_common(M, N, row_stride, dtype, gemma);
+                float eps, int dtype, int flags, hipStream_t stream) {
+  int st = check_common(M, N, row_stride, dtype, flags);
   if (st) return st;
   if (!std::isfinite(eps) || !(eps > 0.0f)) return RMSNORM_E_EPS;
   if (M == 0) return RMSNORM_OK;
@@ -241,10 +241,11 @@ int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t 
   a.nvec = static_cast<int32_t>(N / vec);
   a.eps = eps;
   a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
-  a.w_off = gemma ? 1.0f : 0.0f;
+  a.w_off = (flags & RMSNORM_GEMMA) ? 1.0f : 0.0f;
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
+  a.round_normed = (flags & RMSNORM_ROUND_NORMED) && dtype != RMSNORM_F32;
   return hip_status(launch_fwd(dtype, p, a, stream));
 }
 
@@ -257,16 +258,16 @@ int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t* bytes) 
 }
 
 int rmsnorm_bwd_rows(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx, void* workspace,
-                     size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride, int dtype, int gemma,
+                     size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride, int dtype, int flags,
                      int64_t* partial_rows, hipStream_t stream) {
   if (!partial_rows) return RMSNORM_E_NULL;
   int64_t rows = 0;
-  const int st = check_bwd(x, gamma, dy, rstd, dx, nullptr, workspace, workspace_bytes, M, N, row_stride, dtype, gemma,
+  const int st = check_bwd(x, gamma, dy, rstd, dx, nullptr, workspace, workspace_bytes, M, N, row_stride, dtype, flags,
                            false, &rows);
   if (st) return st;
   *partial_rows = 0;
   if (M == 0) return RMSNORM_OK;
-  return launch_bwd_rows_checked(x, gamma, dy, rstd, dx, workspace, M, N, row_stride, dtype, gemma, partial_rows,
+  return launch_bwd_rows_checked(x, gamma, dy, rstd, dx, workspace, M, N, row_stride, dtype, flags, partial_rows,
                                  stream);
 }
 
@@ -280,13 +281,13 @@ int rmsnorm_dgamma_reduce(const float* partials, int64_t rows, int64_t N, float*
 
 int rmsnorm_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx, float* dgamma,
                 void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride, int dtype,
-                int gemma, hipStream_t stream) {
+                int flags, hipStream_t stream) {
   int64_t rows = 0;
-  int st = check_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, workspace_bytes, M, N, row_stride, dtype, gemma, true,
+  int st = check_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, workspace_bytes, M, N, row_stride, dtype, flags, true,
                      &rows);
   if (st) return st;
   if (M > 0) {
-    st = launch_bwd_rows_checked(x, gamma, dy, rstd, dx, workspace, M, N, row_stride, dtype, gemma, &rows, stream);
+    st = launch_bwd_rows_checked(x, gamma, dy, rstd, dx, workspace, M, N, row_stride, dtype, flags, &rows, stream);
     if (st) return st;
   }
   return launch_reduce_checked(static_cast<const float*>(workspace), rows, N, dgamma, stream);
@@ -299,11 +300,11 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_E_SHAPE: return "invalid shape (need M >= 0 and 1 <= N <= RMSNORM_N_MAX)";
     case RMSNORM_E_STRIDE: return "row stride smaller than N";
     case RMSNORM_E_ALIGN: return "a pointer is not aligned to its element size";
-    case RMSNORM_E_DTYPE: return "unsupported dtype (need RMSNORM_F32 or RMSNORM_BF16)";
+    case RMSNORM_E_DTYPE: return "unsupported dtype (need RMSNORM_F32, RMSNORM_BF16 or RMSNORM_F16)";
     case RMSNORM_E_EPS: return "eps must be finite and > 0";
     case RMSNORM_E_ALIAS: return "an output overlaps another buffer (only dx == dy is allowed)";
     case RMSNORM_E_WORKSPACE: return "workspace smaller than rmsnorm_bwd_workspace_bytes()";
-    case RMSNORM_E_FLAG: return "gemma must be 0 or 1";
+    case RMSNORM_E_FLAG: return "flags may only combine RMSNORM_GEMMA and RMSNORM_ROUND_NORMED";
     case RMSNORM_E_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }

@@ -65,8 +65,8 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
-// VEC consecutive elements with the storage type S (float, or uint16_t for
-// bf16 bits), aligned to their full width so one load/store moves them.  They
+// VEC consecutive elements with the storage type S (float; uint16_t for bf16
+// bits; _Float16), aligned to their full width so one load/store moves them.  They
 // are held as 32-bit words (two bf16 per word) whenever the pack is at least
 // 4 bytes wide.
 template <typename S, int VEC>
@@ -76,10 +76,15 @@ struct alignas(sizeof(S) * VEC) Pack {
   typedef typename std::conditional<(kBytes >= 4), uint32_t, uint16_t>::type Word;
   Word w[kWords];
 
-  // element e as fp32 (bf16 -> fp32 is exact: the bits move to the top half)
+  // element e as fp32 (exact: bf16 bits move to the top half of an fp32;
+  // fp16 converts in hardware)
   __device__ __forceinline__ float get(int e) const {
     if constexpr (sizeof(S) == 4) {
       return __builtin_bit_cast(float, w[e]);
+    } else if constexpr (std::is_same<S, _Float16>::value) {
+      const uint32_t word = kBytes == 2 ? static_cast<uint32_t>(w[0]) : static_cast<uint32_t>(w[e >> 1]);
+      const uint16_t h = static_cast<uint16_t>((e & 1) ? (word >> 16) : word);
+      return static_cast<float>(__builtin_bit_cast(_Float16, h));
     } else if constexpr (kBytes == 2) {
       return __builtin_bit_cast(float, static_cast<uint32_t>(w[0]) << 16);
     } else {
@@ -159,24 +164,39 @@ __device__ __forceinline__ void buf_store_f32(const float (&v)[VEC], Rsrc r, uin
 // ranges are below 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
-// Round VEC fp32 values once (to nearest even; gfx950 converts bf16 pairs in
-// one instruction) to the storage type S.
+// Round VEC fp32 values once (to nearest even; gfx950 converts bf16 and fp16
+// pairs in one instruction each) to the storage type S.
 template <typename S, int VEC>
 __device__ __forceinline__ Pack<S, VEC> round_pack(const float (&o)[VEC]) {
+  typedef typename std::conditional<std::is_same<S, _Float16>::value, _Float16, __bf16>::type H;
+  typedef H h2_t __attribute__((ext_vector_type(2)));
   Pack<S, VEC> p;
   if constexpr (sizeof(S) == 4) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) p.w[e] = __builtin_bit_cast(uint32_t, o[e]);
   } else if constexpr (VEC == 1) {
-    p.w[0] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[0]));
+    p.w[0] = __builtin_bit_cast(uint16_t, static_cast<H>(o[0]));
   } else {
 #pragma unroll
     for (int e = 0; e < VEC; e += 2) {
       const f32x2_t f = {o[e], o[e + 1]};
-      p.w[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+      p.w[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2_t));
     }
   }
   return p;
+}
+
+// v rounded to the storage type S and back (the value a tensor of type S
+// would hold); identity for fp32.
+template <typename S>
+__device__ __forceinline__ float round_to(float v) {
+  if constexpr (sizeof(S) == 4) {
+    return v;
+  } else if constexpr (std::is_same<S, _Float16>::value) {
+    return static_cast<float>(static_cast<_Float16>(v));
+  } else {
+    return static_cast<float>(static_cast<__bf16>(v));
+  }
 }
 
 // v from another lane of the same 16-lane DPP row, selected by CTRL.
@@ -308,7 +328,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
     for (int i = 0; i < ITERS; ++i) {
       float o[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = (xv[i].get(e) * r) * (gv[i].get(e) + a.w_off);
+      for (int e = 0; e < VEC; ++e) {
+        float normed = xv[i].get(e) * r;
+        if (a.round_normed) normed = round_to<S>(normed);  // uniform branch
+        o[e] = normed * (gv[i].get(e) + a.w_off);
+      }
       buf_store<S, VEC, kFwdStoreY>(round_pack<S, VEC>(o), ry, voff + i * iter_bytes);
     }
   }
@@ -564,12 +588,19 @@ hipError_t launch_fwd(int dtype, const RowPlan& p, const FwdArgs& a, hipStream_t
       case 2: return fwd_vec<float, 2>(p, a, s);
       case 4: return fwd_vec<float, 4>(p, a, s);
     }
-  } else {
+  } else if (dtype == 1) {
     switch (p.vec) {
       case 1: return fwd_vec<uint16_t, 1>(p, a, s);
       case 2: return fwd_vec<uint16_t, 2>(p, a, s);
       case 4: return fwd_vec<uint16_t, 4>(p, a, s);
       case 8: return fwd_vec<uint16_t, 8>(p, a, s);
+    }
+  } else if (dtype == 2) {
+    switch (p.vec) {
+      case 1: return fwd_vec<_Float16, 1>(p, a, s);
+      case 2: return fwd_vec<_Float16, 2>(p, a, s);
+      case 4: return fwd_vec<_Float16, 4>(p, a, s);
+      case 8: return fwd_vec<_Float16, 8>(p, a, s);
     }
   }
   return hipErrorInvalidValue;
@@ -582,12 +613,19 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
       case 2: return bwd_vec<float, 2>(p, a, s);
       case 4: return bwd_vec<float, 4>(p, a, s);
     }
-  } else {
+  } else if (dtype == 1) {
     switch (p.vec) {
       case 1: return bwd_vec<uint16_t, 1>(p, a, s);
       case 2: return bwd_vec<uint16_t, 2>(p, a, s);
       case 4: return bwd_vec<uint16_t, 4>(p, a, s);
       case 8: return bwd_vec<uint16_t, 8>(p, a, s);
+    }
+  } else if (dtype == 2) {
+    switch (p.vec) {
+      case 1: return bwd_vec<_Float16, 1>(p, a, s);
+      case 2: return bwd_vec<_Float16, 2>(p, a, s);
+      case 4: return bwd_vec<_Float16, 4>(p, a, s);
+      case 8: return bwd_vec<_Float16, 8>(p, a, s);
     }
   }
   return hipErrorInvalidValue;

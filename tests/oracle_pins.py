@@ -285,4 +285,67 @@ def pin_torch_library(orc):
         assert np.allclose(dg, gt.grad.numpy(), rtol=1e-11, atol=1e-13)
 
 
+# --------------------------------------------------------------------------
+# Rounding to the 16-bit I/O types and the rounded-normalised forward
+# --------------------------------------------------------------------------
+
+def pin_quantize_against_torch_casts(orc):
+    """fp32 values rounded by the oracle equal torch's round-to-nearest-even casts."""
+    import torch
+
+    rng = _rng(29)
+    v = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 1.0, 37.0, 1e3)]).astype(np.float32)
+    for dtype, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        ref = torch.from_numpy(v).to(tdt).double().numpy()
+        got = orc.quantize(v.astype(np.float64), dtype)
+        assert np.array_equal(got, ref), (dtype, np.flatnonzero(got != ref)[:5])
+
+
+def pin_quantize_ties_to_even(orc):
+    """Halfway cases round to the even neighbour (hand-checked against the bit layouts)."""
+    bf = orc.quantize(np.array([1 + 2.0**-8, 1 + 3 * 2.0**-8, -(1 + 2.0**-8), 2 + 2.0**-7, 1 + 2.0**-9]), "bf16")
+    assert np.array_equal(bf, [1.0, 1 + 2.0**-6, -1.0, 2.0, 1.0]), bf
+    hf = orc.quantize(np.array([1 + 2.0**-11, 1 + 3 * 2.0**-11, 1 + 2.0**-12, 65504.0]), "f16")
+    assert np.array_equal(hf, [1.0, 1 + 2.0**-9, 1.0, 65504.0]), hf
+
+
+def pin_normed_rounded_unit_weight(orc):
+    """With w = 1 the two roundings collapse to one: T(T(x r) * 1) = T(x r)."""
+    rng = _rng(31)
+    x = rng.standard_normal((9, 70))
+    for dtype in ("bf16", "f16"):
+        y1, r1 = orc.forward_normed_rounded(x, np.ones(70), 1e-6, False, dtype)
+        y0, r0 = orc.forward(x, np.ones(70), 1e-6)
+        assert np.array_equal(y1, orc.quantize(y0, dtype)) and np.array_equal(r1, r0)
+        # Gemma with gamma = 0 is the same unit weight
+        y2, _ = orc.forward_normed_rounded(x, np.zeros(70), 1e-6, True, dtype)
+        assert np.array_equal(y2, y1)
+
+
+def pin_normed_rounded_against_torch(orc):
+    """The Hugging Face order computed with torch on the CPU: normed (fp64 -> fp32 -> T), times the
+    weight in T (torch multiplies 16-bit tensors in fp32 and rounds once).  Equal everywhere except
+    where torch's fp32 intermediate lands exactly on a tie of T (double rounding; about one element
+    in 2^16 for bf16, 2^13 for fp16), where the oracle rounds the exact value once."""
+    import torch
+
+    rng = _rng(37)
+    x = rng.standard_normal((64, 512))
+    bits = {"bf16": 8, "f16": 11}
+    for dtype, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        gamma = torch.from_numpy(rng.uniform(0.5, 1.5, 512)).to(tdt)
+        xt = torch.from_numpy(x)
+        normed32 = (xt * torch.rsqrt(xt.square().mean(-1, keepdim=True) + 1e-6)).to(torch.float32)
+        ref = (normed32.to(tdt) * gamma).double().numpy()
+        got, _ = orc.forward_normed_rounded(x, gamma.double().numpy(), 1e-6, False, dtype)
+        bad = np.flatnonzero(got != ref)
+        m, _ = np.frexp(normed32.double().numpy().ravel()[bad])
+        frac = np.abs(m) * 2.0 ** bits[dtype]
+        assert np.all(frac - np.floor(frac) == 0.5), (dtype, bad)  # every mismatch is a tie in fp32
+        assert len(bad) <= 8, (dtype, len(bad))
+        # and it is a different function from one rounding of x r w
+        single = orc.quantize(orc.forward(x, gamma.double().numpy(), 1e-6)[0], dtype)
+        assert np.mean(single != got) > 0.05
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -17,6 +17,9 @@ Tolerances (written here, applied per element):
   over rows of ``|sum dx x| / (||dx|| ||x||) <= 1e-3``; for shorter rows the
   bf16 rounding of dx alone moves this ratio by ~2^-9/sqrt(N)).  A kernel that
   drops the r^3 term fails both.
+* fp16 I/O: y and dx within the tutorial's fp16 rule (Triton RMSNorm tutorial,
+  "Ba so sánh số học riêng biệt": allclose with atol = rtol = 3e-3), plus the
+  same norm-wise and invariant guards as bf16; dgamma (fp32) within 1e-3.
 * r (rstd): relative error <= 2e-6 against the oracle's r in every row.
 
 dx is the difference of two terms, r*u and x*r^3*m.  Where they cancel (a
@@ -60,7 +63,7 @@ def check_close(name: str, g: np.ndarray, o: np.ndarray, dtype: str, kind: str, 
         diag["max_rel"] = float(rel.max())
         assert rel.max() <= eps, f"{name}: max rel err {rel.max():.3g} > {eps} at {worst}: {g[worst]} vs {o[worst]}"
     else:
-        bound = 2e-2 + 1.6e-2 * np.abs(o)
+        bound = 2e-2 + 1.6e-2 * np.abs(o) if dtype == "bf16" else 3e-3 + 3e-3 * np.abs(o)
         err = np.abs(g - o)
         worst = np.unravel_index(np.argmax(err - bound), err.shape)
         assert np.all(err <= bound), f"{name}: |g-o| {err[worst]:.3g} > {bound[worst]:.3g} at {worst}"
@@ -147,7 +150,7 @@ def compare_with_oracle(run: Run, rows: np.ndarray | None = None) -> dict:
     check_rstd(f"{w.name} rstd", r[sel], r_o[sel])
     direct = r_o[:, None] * dy * oracle.weight(gamma, w.gemma)[None, :]
     diag["dx"] = check_close(f"{w.name} dx", dx[sel], dx_o[sel], w.dtype, "dx", direct=direct[sel])
-    if w.dtype == "bf16" and w.N >= 64:
+    if w.dtype != "f32" and w.N >= 64:
         diag["dx_invariant"] = check_dx_invariant(f"{w.name} dx", dx[sel], x[sel])
     diag["dgamma"] = check_close(f"{w.name} dgamma", dg, dg_o, w.dtype, "dgamma")
     return diag

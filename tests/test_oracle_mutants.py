@@ -41,6 +41,12 @@ MUTANTS = {
     "dgamma_uses_u": ("dgamma = dgamma_from_rows(dy * x * r[:, None])", "dgamma = dgamma_from_rows(u * x * r[:, None])"),
     "dgamma_mean_not_sum": ("return np.sum(_f64(contributions), axis=0)", "return np.mean(_f64(contributions), axis=0)"),
     "dgamma_sums_columns": ("return np.sum(_f64(contributions), axis=0)", "return np.sum(_f64(contributions), axis=1)"),
+    "quantize_truncates": ("return np.ldexp(np.round(m * 2.0**p), e - p)", "return np.ldexp(np.floor(m * 2.0**p), e - p)"),
+    "quantize_bf16_bits": ('_SIGNIFICAND_BITS = {"bf16": 8,', '_SIGNIFICAND_BITS = {"bf16": 7,'),
+    "quantize_f16_as_f32": ("return v.astype(np.float16).astype(np.float64)", "return v.astype(np.float32).astype(np.float64)"),
+    "normed_not_rounded": ("normed = quantize(x * r[:, None], dtype)", "normed = x * r[:, None]"),
+    "product_not_rounded": ("return quantize(normed * w[None, :], dtype), r", "return normed * w[None, :], r"),
+    "normed_weight_dropped": ("return quantize(normed * w[None, :], dtype), r", "return quantize(normed, dtype), r"),
 }
 
 

@@ -82,6 +82,12 @@ SMALL = [
     ("bf16", 2, 12288, False, False),
     ("bf16", 9, 6, False, False),       # 4-byte vectors (3 per row)
     ("f32", 11, 10, False, False),      # 8-byte fp32 vectors
+    ("f16", 17, 257, False, False),     # fp16 I/O
+    ("f16", 33, 1000, True, False),
+    ("f16", 257, 8192, True, True),
+    ("f16", 100, 16384, False, False),
+    ("f16", 4096, 4096, False, False),
+    ("f16", 7, 12, False, True),
 ]
 
 
@@ -186,3 +192,31 @@ def test_rejections_do_not_write():
         rn.rmsnorm_fwd(x, g, x, r)
     torch.cuda.synchronize()
     assert torch.all(y == 3.0) and torch.all(r == 5.0)
+
+
+# ---------------------------------------------------------------------------
+# The Hugging Face rounding order (normalised value rounded before the weight
+# multiply), against oracle.forward_normed_rounded.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,M,N,gemma", [("bf16", 300, 1000, False), ("f16", 300, 1000, False),
+                                             ("bf16", 64, 8192, True), ("f16", 33, 257, False)])
+def test_round_normed_order(dtype, M, N, gemma):
+    w = (wl.C3 if gemma else wl.C2).scaled(M=M, N=N, dtype=dtype, gemma=gemma, seed=7 * M + N)
+    t = wl.make_inputs(w)
+    x, g = t["x"].cuda(), t["gamma"].cuda()
+    outs = {}
+    for rn_flag in (True, False):
+        y = torch.empty_like(x)
+        r = torch.empty(M, dtype=torch.float32, device="cuda")
+        rn.rmsnorm_fwd(x, g, y, r, eps=w.eps, gemma=gemma, round_normed=rn_flag)
+        torch.cuda.synchronize()
+        outs[rn_flag] = wl.to_f64(y)
+    xs, gs = wl.to_f64(t["x"]), wl.to_f64(t["gamma"])
+    hf, _ = oracle.forward_normed_rounded(xs, gs, w.eps, gemma, dtype)
+    single = oracle.quantize(oracle.forward(xs, gs, w.eps, gemma)[0], dtype)
+    ulp = np.abs(oracle.quantize(hf * (1 + 2.0 ** -7), dtype) - hf) + 1e-30
+    # exact except where fp32 vs fp64 r flips the inner rounding: then one unit in the last place
+    assert np.mean(outs[True] == hf) >= 0.999, np.mean(outs[True] == hf)
+    assert np.all(np.abs(outs[True] - hf) <= ulp)
+    assert np.mean(outs[False] == single) >= 0.999
+    assert np.mean(outs[True] != outs[False]) > 0.02  # the flag changes the result

@@ -16,7 +16,8 @@ Recipe (the same for every workload):
   of the row indices: the first ``n_scaled`` rows of it are multiplied by 100
   (in float32, before quantisation), the next ``n_zero`` rows are zeroed, so
   the two sets are disjoint and their sizes exact.
-* Quantisation to bf16 uses torch's round-to-nearest-even cast on the CPU.
+* Quantisation to bf16 or fp16 uses torch's round-to-nearest-even cast on
+  the CPU.
   The quantised tensors are the canonical inputs: the oracle upcasts them
   exactly to float64, the GPU receives the same bits.
 
@@ -30,7 +31,7 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclass(frozen=True)
