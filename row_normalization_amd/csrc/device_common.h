@@ -1,0 +1,227 @@
+// Device-side building blocks shared by the row kernels (RMSNorm and
+// LayerNorm): packed row vectors, raw-buffer access with hardware range
+// checks, rounding to the I/O types, and the wave / row-group reductions.
+// Included by the .hip files only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "launch.h"
+
+namespace rmsn {
+namespace dev {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family:
+// 32-bit data format; the range check is then offset against the byte count.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy operand of buffer instructions: 0 = default, 2 = nontemporal.
+constexpr int kDefault = 0;
+constexpr int kNontemporal = 2;
+
+// A descriptor for `bytes` bytes at `base`; accesses at or past `bytes` read
+// zero and write nothing.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+// VEC consecutive elements with the storage type S (float; uint16_t for bf16
+// bits; _Float16), aligned to their full width so one load/store moves them.  They
+// are held as 32-bit words (two bf16 per word) whenever the pack is at least
+// 4 bytes wide.
+template <typename S, int VEC>
+struct alignas(sizeof(S) * VEC) Pack {
+  static constexpr int kBytes = int(sizeof(S)) * VEC;
+  static constexpr int kWords = kBytes >= 4 ? kBytes / 4 : 1;
+  typedef typename std::conditional<(kBytes >= 4), uint32_t, uint16_t>::type Word;
+  Word w[kWords];
+
+  // element e as fp32 (exact: bf16 bits move to the top half of an fp32;
+  // fp16 converts in hardware)
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (sizeof(S) == 4) {
+      return __builtin_bit_cast(float, w[e]);
+    } else if constexpr (std::is_same<S, _Float16>::value) {
+      const uint32_t word = kBytes == 2 ? static_cast<uint32_t>(w[0]) : static_cast<uint32_t>(w[e >> 1]);
+      const uint16_t h = static_cast<uint16_t>((e & 1) ? (word >> 16) : word);
+      return static_cast<float>(__builtin_bit_cast(_Float16, h));
+    } else if constexpr (kBytes == 2) {
+      return __builtin_bit_cast(float, static_cast<uint32_t>(w[0]) << 16);
+    } else {
+      const uint32_t word = w[e >> 1];
+      return __builtin_bit_cast(float, (e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+    }
+  }
+
+  // Makes the compiler treat the words as changed here, so it re-derives the
+  // fp32 values from the packed words after this point instead of keeping a
+  // second, unpacked copy of the row alive across the row reduction (which
+  // would double the registers a lane needs).  Emits no instruction.
+  __device__ __forceinline__ void keep_packed() {
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) {
+      if constexpr (sizeof(Word) == 4) {
+        asm volatile("" : "+v"(w[k]));
+      } else {
+        uint32_t t = w[k];
+        asm volatile("" : "+v"(t));
+        w[k] = static_cast<Word>(t);
+      }
+    }
+  }
+};
+
+// One pack from a buffer at byte offset `off`.  The whole offset goes in the
+// instruction's vector offset, which the range check covers (the scalar
+// offset operand is left at zero: it is added to the address but not checked).
+template <typename S, int VEC, int AUX>
+__device__ __forceinline__ Pack<S, VEC> buf_load(Rsrc r, uint32_t off) {
+  typedef Pack<S, VEC> P;
+  if constexpr (P::kBytes == 16) {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+  } else if constexpr (P::kBytes == 8) {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+  } else if constexpr (P::kBytes == 4) {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
+  } else {
+    return __builtin_bit_cast(P, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX));
+  }
+}
+
+template <typename S, int VEC, int AUX>
+__device__ __forceinline__ void buf_store(const Pack<S, VEC>& p, Rsrc r, uint32_t off) {
+  typedef Pack<S, VEC> P;
+  if constexpr (P::kBytes == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, p), r, off, 0, AUX);
+  } else if constexpr (P::kBytes == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, p), r, off, 0, AUX);
+  } else if constexpr (P::kBytes == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p), r, off, 0, AUX);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, p), r, off, 0, AUX);
+  }
+}
+
+// VEC fp32 values at byte offset `off`, in stores of at most 16 bytes.
+template <int VEC, int AUX>
+__device__ __forceinline__ void buf_store_f32(const float (&v)[VEC], Rsrc r, uint32_t off) {
+  if constexpr (VEC > 4) {
+#pragma unroll
+    for (int k = 0; k < VEC; k += 4) {
+      const u32x4_t q = {__builtin_bit_cast(uint32_t, v[k]), __builtin_bit_cast(uint32_t, v[k + 1]),
+                         __builtin_bit_cast(uint32_t, v[k + 2]), __builtin_bit_cast(uint32_t, v[k + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(q, r, off + k * 4u, 0, AUX);
+    }
+  } else {
+    Pack<float, VEC> p;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p.w[e] = __builtin_bit_cast(uint32_t, v[e]);
+    buf_store<float, VEC, AUX>(p, r, off);
+  }
+}
+
+// Byte offset that is out of range of every descriptor made here (their
+// ranges are below 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+// Round VEC fp32 values once (to nearest even; gfx950 converts bf16 and fp16
+// pairs in one instruction each) to the storage type S.
+template <typename S, int VEC>
+__device__ __forceinline__ Pack<S, VEC> round_pack(const float (&o)[VEC]) {
+  typedef typename std::conditional<std::is_same<S, _Float16>::value, _Float16, __bf16>::type H;
+  typedef H h2_t __attribute__((ext_vector_type(2)));
+  Pack<S, VEC> p;
+  if constexpr (sizeof(S) == 4) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p.w[e] = __builtin_bit_cast(uint32_t, o[e]);
+  } else if constexpr (VEC == 1) {
+    p.w[0] = __builtin_bit_cast(uint16_t, static_cast<H>(o[0]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; e += 2) {
+      const f32x2_t f = {o[e], o[e + 1]};
+      p.w[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2_t));
+    }
+  }
+  return p;
+}
+
+// v rounded to the storage type S and back (the value a tensor of type S
+// would hold); identity for fp32.
+template <typename S>
+__device__ __forceinline__ float round_to(float v) {
+  if constexpr (sizeof(S) == 4) {
+    return v;
+  } else if constexpr (std::is_same<S, _Float16>::value) {
+    return static_cast<float>(static_cast<_Float16>(v));
+  } else {
+    return static_cast<float>(static_cast<__bf16>(v));
+  }
+}
+
+// v from another lane of the same 16-lane DPP row, selected by CTRL.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the same total.
+// quad_perm swaps (xor 1, xor 2), row_half_mirror and row_mirror complete
+// the 16-lane rows, a ds_swizzle swaps 16-lane rows inside each 32-lane
+// half, and the two halves are added through scalar readlanes.  The order of
+// the additions is fixed, so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // lane ^ 16
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  return lo + hi;
+}
+
+// Sum of one value per wave over the `wpr` waves of a row group, through LDS.
+// Every wave of the group reads the slots in the same order.
+__device__ __forceinline__ float group_sum(float wave_total, float (*red)[kMaxBlockWaves], int64_t step, int wave,
+                                          int group, int wpr, int lane) {
+  float* slot = red[step & 1];
+  if (lane == 0) slot[wave] = wave_total;
+  __syncthreads();
+  float t = 0.f;
+  for (int k = 0; k < wpr; ++k) t += slot[group * wpr + k];
+  return t;
+}
+
+// Where a lane sits: its wave (uniform, in a scalar register), the row group
+// of the wave and the wave within the group.
+struct Lane {
+  int lane, wave, group, wv;
+  __device__ __forceinline__ explicit Lane(int wpr) {
+    lane = threadIdx.x & (kWave - 1);
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    group = wave / wpr;
+    wv = wave - group * wpr;
+  }
+  // index of the lane's first column vector in a row
+  __device__ __forceinline__ uint32_t first_vec() const { return static_cast<uint32_t>(wv * kWave + lane); }
+};
+
+// Row handled by row group `group` of this workgroup at step `step` (of
+// `row_iters`): at each step the workgroups cover consecutive rows, so the
+// rows in flight across the chip form one compact window.
+__device__ __forceinline__ int64_t row_of(int64_t step, int64_t row_iters, int rpb, int group) {
+  (void)row_iters;
+  return (step * gridDim.x + blockIdx.x) * rpb + group;
+}
+
+}  // namespace dev
+}  // namespace rmsn
