@@ -11,9 +11,11 @@ import types
 
 import pytest
 
-from tests import oracle_pins
+from tests import oracle_pins, oracle_pins_ln
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "rmsnorm_oracle.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "rmsnorm_oracle.py")
+LN_SRC = os.path.join(ORACLE_DIR, "layernorm_oracle.py")
 
 MUTANTS = {
     "denominator_n_plus_1": ("mean_sq = np.sum(x * x, axis=1) / n", "mean_sq = np.sum(x * x, axis=1) / (n + 1)"),
@@ -50,8 +52,45 @@ MUTANTS = {
 }
 
 
-def _load_mutant(name, old, new):
-    with open(SRC) as f:
+LN_MUTANTS = {
+    "ln_mean_denominator": ("mean = np.sum(x, axis=1) / n", "mean = np.sum(x, axis=1) / (n + 1)"),
+    "ln_mean_rows_for_columns": ("    n = x.shape[1]\n    mean = np.sum", "    n = x.shape[0]\n    mean = np.sum"),
+    "ln_var_unbiased": ("var = np.sum(diff * diff, axis=1) / n", "var = np.sum(diff * diff, axis=1) / (n - 1)"),
+    "ln_var_one_pass": ("var = np.sum(diff * diff, axis=1) / n",
+                        "var = np.sum(x * x, axis=1) / n - mean * mean"),
+    "ln_var_not_centred": ("diff = x - mean[:, None]", "diff = x"),
+    "ln_eps_outside_root": ("rstd = 1.0 / np.sqrt(var + eps)\n    x_hat = (x - mean[:, None]) * rstd[:, None]\n    y",
+                            "rstd = 1.0 / np.sqrt(var) + eps\n    x_hat = (x - mean[:, None]) * rstd[:, None]\n    y"),
+    "ln_std_not_inverse": ("rstd = 1.0 / np.sqrt(var + eps)\n    x_hat = (x - mean[:, None]) * rstd[:, None]\n    y",
+                           "rstd = np.sqrt(var + eps)\n    x_hat = (x - mean[:, None]) * rstd[:, None]\n    y"),
+    "ln_fwd_mean_not_subtracted": ("x_hat = (x - mean[:, None]) * rstd[:, None]\n    y",
+                                   "x_hat = x * rstd[:, None]\n    y"),
+    "ln_fwd_drops_bias": ("y = x_hat * _f64(w)[None, :] + _f64(b)[None, :]", "y = x_hat * _f64(w)[None, :]"),
+    "ln_fwd_bias_times_weight": ("y = x_hat * _f64(w)[None, :] + _f64(b)[None, :]",
+                                 "y = (x_hat + _f64(b)[None, :]) * _f64(w)[None, :]"),
+    "ln_bwd_eps_dropped": ("rstd = 1.0 / np.sqrt(var + eps)\n    x_hat = (x - mean[:, None]) * rstd[:, None]\n    g",
+                           "rstd = 1.0 / np.sqrt(var)\n    x_hat = (x - mean[:, None]) * rstd[:, None]\n    g"),
+    "ln_bwd_mean_not_subtracted": ("x_hat = (x - mean[:, None]) * rstd[:, None]\n    g",
+                                   "x_hat = x * rstd[:, None]\n    g"),
+    "ln_g_drops_weight": ("g = _f64(w)[None, :] * dy", "g = dy"),
+    "ln_c1_sum_not_mean": ("c1 = np.sum(x_hat * g, axis=1) / n", "c1 = np.sum(x_hat * g, axis=1)"),
+    "ln_c1_wrong_operand": ("c1 = np.sum(x_hat * g, axis=1) / n", "c1 = np.sum(x_hat * dy, axis=1) / n"),
+    "ln_c2_sum_not_mean": ("c2 = np.sum(g, axis=1) / n", "c2 = np.sum(g, axis=1)"),
+    "ln_c2_dropped": ("(x_hat * c1[:, None] + c2[:, None])", "(x_hat * c1[:, None])"),
+    "ln_c1_dropped": ("(x_hat * c1[:, None] + c2[:, None])", "(c2[:, None])"),
+    "ln_c2_sign": ("(x_hat * c1[:, None] + c2[:, None])", "(x_hat * c1[:, None] - c2[:, None])"),
+    "ln_dx_no_rstd": ("dx = (g - (x_hat * c1[:, None] + c2[:, None])) * rstd[:, None]",
+                      "dx = (g - (x_hat * c1[:, None] + c2[:, None]))"),
+    "ln_dw_not_normalised": ("dw = column_sums(dy * x_hat)", "dw = column_sums(dy * x)"),
+    "ln_dw_includes_weight": ("dw = column_sums(dy * x_hat)", "dw = column_sums(g * x_hat)"),
+    "ln_db_includes_weight": ("db = column_sums(dy)", "db = column_sums(g)"),
+    "ln_sums_are_means": ("return np.sum(_f64(contributions), axis=0)", "return np.mean(_f64(contributions), axis=0)"),
+    "ln_sums_over_columns": ("return np.sum(_f64(contributions), axis=0)", "return np.sum(_f64(contributions), axis=1)"),
+}
+
+
+def _load_mutant(name, old, new, src_path=SRC):
+    with open(src_path) as f:
         src = f.read()
     assert src.count(old) == 1, f"mutation {name!r} does not match the oracle source exactly once"
     mod = types.ModuleType(f"oracle_mutant_{name}")
@@ -69,3 +108,15 @@ def test_mutant_is_caught(name):
         except Exception as e:  # an assertion or a shape error both reject the mutant
             caught.append((pin.__name__, type(e).__name__))
     assert caught, f"no pin rejects the mutant {name!r}"
+
+
+@pytest.mark.parametrize("name", sorted(LN_MUTANTS))
+def test_layernorm_mutant_is_caught(name):
+    mod = _load_mutant(name, *LN_MUTANTS[name], src_path=LN_SRC)
+    caught = []
+    for pin in oracle_pins_ln.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin rejects the LayerNorm mutant {name!r}"

@@ -48,3 +48,27 @@ def test_algorithmic_bytes_table():
         "fwd": 536_952_832, "bwd_rows": 805_388_288, "bwd": 805_421_056, "fwd_bwd": 1_342_373_888}
     assert wl.algorithmic_bytes(64, 128, 4)["fwd_bwd"] == 165_888
     assert wl.algorithmic_bytes(32768, 5120, 2)["fwd_bwd"] == 1_678_024_704
+
+
+def test_layernorm_inputs():
+    w = wl.LN1.scaled(M=256, N=1024)
+    t = wl.make_inputs(w)
+    assert sorted(t) == ["beta", "dy", "gamma", "x"]
+    assert all(v.dtype == torch.float16 for v in t.values())
+    x, g, b, dy = (wl.to_f64(t[k]) for k in ("x", "gamma", "beta", "dy"))
+    assert abs(x.mean() + 2.3) < 0.01 and abs(x.std() - 0.5) < 0.01
+    assert g.min() >= 0 and g.max() <= 1 and b.min() >= 0 and b.max() <= 1
+    assert not np.array_equal(g, b)  # weight and bias come from different streams
+    assert abs(dy.std() - 0.1) < 0.002
+    # the bias stream leaves the other inputs as an RMSNorm workload draws them
+    r = wl.make_inputs(wl.Workload("same", "f16", 256, 1024, x=w.x, gamma=w.gamma, dy=w.dy))
+    for k in ("x", "gamma", "dy"):
+        assert torch.equal(r[k].view(torch.int16), t[k].view(torch.int16))
+    assert wl.LN_SWEEP_NS[0] == 1024 and wl.LN_SWEEP_NS[-1] == 15872 and len(wl.LN_SWEEP_NS) == 30
+    assert wl.ln_sweep(2048).M == 4096 and wl.ln_sweep(2048).eps == 1e-5
+
+
+def test_layernorm_algorithmic_bytes():
+    # fwd = 2MNb + 2Nb + 8M; bwd = 3MNb + Nb + 8M + 8N
+    assert wl.ln_algorithmic_bytes(4096, 8192, 2) == {
+        "fwd": 134_283_264, "bwd_rows": 201_375_744, "bwd": 201_441_280, "fwd_bwd": 335_724_544}

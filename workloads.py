@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the RMSNorm forward/backward path.
+"""Seeded synthetic inputs for the RMSNorm and LayerNorm forward/backward paths.
 
 This module is shared by the tests, ``bench.py`` and ``__graft_entry__.smoke()``:
 it feeds the same quantised inputs to the fp64 CPU oracle and to the HIP
@@ -12,6 +12,9 @@ Recipe (the same for every workload):
   streams, one each for x, gamma, dy and the choice of special rows.
 * Values are drawn in float32 (``standard_normal``/``random`` with
   ``dtype=float32``), then shifted and scaled in float32.
+* LayerNorm workloads also draw a bias from a fifth stream
+  (``spawn(5)[4]``; the first four children of ``spawn(5)`` are those of
+  ``spawn(4)``, so adding it changes no other input).
 * Special rows (scaled by 100 / set to zero) are chosen from one permutation
   of the row indices: the first ``n_scaled`` rows of it are multiplied by 100
   (in float32, before quantisation), the next ``n_zero`` rows are zeroed, so
@@ -36,10 +39,11 @@ DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 @dataclass(frozen=True)
 class Workload:
-    """One synthetic RMSNorm problem: shape, dtype and input distributions.
+    """One synthetic problem: shape, dtype and input distributions.
 
-    ``x``, ``gamma`` and ``dy`` are ``("normal", mean, std)`` or
-    ``("uniform", low, high)``.
+    ``x``, ``gamma`` (the weight), ``dy`` and ``beta`` (the LayerNorm bias;
+    None for RMSNorm) are ``("normal", mean, std)`` or ``("uniform", low,
+    high)``.
     """
 
     name: str
@@ -55,6 +59,7 @@ class Workload:
     scaled_row_frac: float = 0.0
     zero_row_frac: float = 0.0
     seed: int = 0
+    beta: tuple | None = None
     note: str = field(default="", compare=False)
 
     @property
@@ -95,6 +100,24 @@ C5 = Workload("c5_bf16_8192x16384", "bf16", 8192, 16384, gamma=("normal", 1.0, 0
 CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
 HEADLINE = C3
 
+# LayerNorm workloads, with the distributions of the LayerNorm chapter's unit
+# test and benchmark: x = -2.3 + 0.5 N(0,1), weight and bias U(0,1),
+# dy = 0.1 N(0,1), eps 1e-5, fp16.
+_LN = dict(x=("normal", -2.3, 0.5), gamma=("uniform", 0.0, 1.0), beta=("uniform", 0.0, 1.0),
+           dy=("normal", 0.0, 0.1), eps=1e-5)
+LN1 = Workload("ln1_f16_1151x8192", "f16", 1151, 8192, note="the chapter's unit-test shape", **_LN)
+# its GB/s sweep: M = 4096, N = 512 * i for i = 2 .. 31
+LN_SWEEP_M = 4096
+LN_SWEEP_NS = tuple(512 * i for i in range(2, 32))
+
+
+def ln_sweep(N: int) -> Workload:
+    """One point of the LayerNorm bandwidth sweep (M = 4096, fp16)."""
+    return Workload(f"ln_f16_{LN_SWEEP_M}x{N}", "f16", LN_SWEEP_M, N, note="GB/s sweep point", **_LN)
+
+
+LN_CONFIGS = {"ln1": LN1, "ln_sweep_8192": ln_sweep(8192)}
+
 
 def _draw(rng: np.random.Generator, spec: tuple, shape) -> np.ndarray:
     kind, a, b = spec
@@ -124,8 +147,9 @@ def special_rows(w: Workload) -> tuple[np.ndarray, np.ndarray]:
 
 
 def make_inputs(w: Workload) -> dict[str, torch.Tensor]:
-    """Quantised CPU tensors ``x [M,N]``, ``gamma [N]``, ``dy [M,N]`` in ``w.dtype``."""
-    ss = np.random.SeedSequence(w.seed).spawn(4)
+    """Quantised CPU tensors ``x [M,N]``, ``gamma [N]``, ``dy [M,N]`` (and
+    ``beta [N]`` for a LayerNorm workload) in ``w.dtype``."""
+    ss = np.random.SeedSequence(w.seed).spawn(5)
     rx, rg, rdy = (np.random.Generator(np.random.PCG64(s)) for s in ss[:3])
     x = _draw(rx, w.x, (w.M, w.N))
     gamma = _draw(rg, w.gamma, (w.N,))
@@ -135,8 +159,11 @@ def make_inputs(w: Workload) -> dict[str, torch.Tensor]:
         x[scaled] *= np.float32(100.0)
     if zero.size:
         x[zero] = 0.0
+    arrays = [("x", x), ("gamma", gamma), ("dy", dy)]
+    if w.beta is not None:
+        arrays.append(("beta", _draw(np.random.Generator(np.random.PCG64(ss[4])), w.beta, (w.N,))))
     out = {}
-    for k, a in (("x", x), ("gamma", gamma), ("dy", dy)):
+    for k, a in arrays:
         t = torch.from_numpy(a)
         out[k] = t if w.dtype == "f32" else t.to(w.torch_dtype)
     return out
@@ -152,6 +179,18 @@ def algorithmic_bytes(M: int, N: int, elsize: int) -> dict[str, int]:
     fwd = 2 * M * N * elsize + N * elsize + 4 * M
     bwd_rows = 3 * M * N * elsize + N * elsize + 4 * M
     bwd = bwd_rows + 4 * N
+    return {"fwd": fwd, "bwd_rows": bwd_rows, "bwd": bwd, "fwd_bwd": fwd + bwd}
+
+
+def ln_algorithmic_bytes(M: int, N: int, elsize: int) -> dict[str, int]:
+    """LayerNorm's algorithmic bytes.  fwd reads x, weight and bias, writes y,
+    mean and rstd (fp32 per row); bwd reads x, dy, weight, mean and rstd,
+    writes dx and the fp32 dw and db.  (The chapter's own GB/s figures count
+    2 * numel * elsize for the forward and 3 * numel * elsize for the
+    backward: the same up to the O(M + N) terms.)"""
+    fwd = 2 * M * N * elsize + 2 * N * elsize + 8 * M
+    bwd_rows = 3 * M * N * elsize + N * elsize + 8 * M
+    bwd = bwd_rows + 8 * N
     return {"fwd": fwd, "bwd_rows": bwd_rows, "bwd": bwd, "fwd_bwd": fwd + bwd}
 
 
