@@ -11,7 +11,11 @@ Prints ONE JSON line.  ``value`` is algorithmic bytes of fwd+bwd per step
 divided by the measured step time; ``roofline`` describes the dominant kernel
 (the backward row pass) timed per launch with HIP events on the same stream;
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
-workload on this host.
+workload on this host.  ``layernorm`` holds the LayerNorm sweep of the
+LayerNorm chapter's benchmark (M = 4096, fp16, N = 1024 .. 15872): per point,
+the forward and the backward (row pass + dw/db reduction) timed per launch
+with events, as GB/s by the chapter's formulas (2 and 3 * numel * elsize per
+launch) and as a fraction of the HBM peak on algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -33,6 +37,7 @@ import torch  # noqa: E402
 import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
 METRIC = "RMSNorm fwd+bwd achieved HBM GB/s and % of peak, bf16 M=16384 N=8192"
 KERNEL_SRC = os.path.join(ROOT, "row_normalization_amd", "csrc", "rmsnorm_kernels.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md")
@@ -46,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="c3", choices=sorted(wl.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
+    ap.add_argument("--ln-steps", type=int, default=50, help="timed launches per LayerNorm sweep point")
     return ap.parse_args()
 
 
@@ -86,7 +93,7 @@ class Path:
         self.dgamma = torch.empty(w.N, dtype=torch.float32, device=dev)
         self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(w.M, w.N, w.torch_dtype)
         self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device=dev)
-        self.dtype = 0 if w.dtype == "f32" else 1
+        self.dtype = DTYPE_CODE[w.dtype]
         self.stream = torch.cuda.current_stream().cuda_stream
         self.rows = ctypes_int64()
         self.partial_rows = None
@@ -125,6 +132,86 @@ class ctypes_int64:
     @property
     def value(self):
         return self._v.value
+
+
+class LnPath:
+    """Device buffers and C-ABI calls of the LayerNorm path for one workload."""
+
+    def __init__(self, w: wl.Workload):
+        import row_normalization_amd as rn
+
+        self.w = w
+        self.L = rn.lib()
+        t = wl.make_inputs(w)
+        self.x, self.weight, self.bias, self.dy = (t[k].to("cuda") for k in ("x", "gamma", "beta", "dy"))
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.mean = torch.empty(w.M, dtype=torch.float32, device="cuda")
+        self.rstd = torch.empty(w.M, dtype=torch.float32, device="cuda")
+        self.dw = torch.empty(w.N, dtype=torch.float32, device="cuda")
+        self.db = torch.empty(w.N, dtype=torch.float32, device="cuda")
+        self.ws_bytes = rn.layernorm_bwd_workspace_bytes(w.M, w.N, w.torch_dtype)
+        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device="cuda")
+        self.dtype = DTYPE_CODE[w.dtype]
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.rows = ctypes_int64()
+        self.partial_rows = None
+
+    def fwd(self):
+        st = self.L.layernorm_fwd(self.x.data_ptr(), self.weight.data_ptr(), self.bias.data_ptr(), self.y.data_ptr(),
+                                  self.mean.data_ptr(), self.rstd.data_ptr(), self.w.M, self.w.N, self.w.N,
+                                  self.w.eps, self.dtype, self.stream)
+        assert st == 0, st
+
+    def bwd_rows(self):
+        st = self.L.layernorm_bwd_rows(self.x.data_ptr(), self.weight.data_ptr(), self.dy.data_ptr(),
+                                       self.mean.data_ptr(), self.rstd.data_ptr(), self.dx.data_ptr(),
+                                       self.ws.data_ptr(), self.ws_bytes, self.w.M, self.w.N, self.w.N, self.dtype,
+                                       self.rows.ref, self.stream)
+        assert st == 0, st
+        self.partial_rows = self.rows.value
+
+    def reduce(self):
+        st = self.L.layernorm_dwdb_reduce(self.ws.data_ptr(), self.partial_rows, self.w.N, self.dw.data_ptr(),
+                                          self.db.data_ptr(), self.stream)
+        assert st == 0, st
+
+    def step(self):
+        self.fwd()
+        self.bwd_rows()
+        self.reduce()
+
+
+def layernorm_sweep(steps: int) -> dict:
+    """The LayerNorm chapter's sweep: M = 4096 fp16, N = 512 * i, i = 2 .. 31."""
+    points = []
+    for N in wl.LN_SWEEP_NS:
+        w = wl.ln_sweep(N)
+        path = LnPath(w)
+        for _ in range(3):
+            path.step()
+        k = time_kernels(path, steps)
+        t_f, t_r, t_d = (k[n]["mean_s"] for n in ("fwd", "bwd_rows", "dgamma_reduce"))
+        b = wl.ln_algorithmic_bytes(w.M, w.N, w.elsize)
+        numel_bytes = w.M * w.N * w.elsize
+        points.append({
+            "N": N,
+            "fwd_us": round(t_f * 1e6, 2), "bwd_rows_us": round(t_r * 1e6, 2), "reduce_us": round(t_d * 1e6, 2),
+            "fwd_gbps_page_formula": round(2 * numel_bytes / t_f / 1e9, 1),
+            "bwd_gbps_page_formula": round(3 * numel_bytes / (t_r + t_d) / 1e9, 1),
+            "fwd_frac": round(b["fwd"] / t_f / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_rows_frac": round(b["bwd_rows"] / t_r / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_frac": round(b["bwd"] / (t_r + t_d) / 1e9 / PEAK_HBM_GBPS, 4),
+            "partial_rows": path.partial_rows,
+        })
+        print(f"[layernorm sweep] N={N}: fwd {points[-1]['fwd_us']} us, bwd {t_r * 1e6 + t_d * 1e6:.1f} us",
+              file=sys.stderr, flush=True)
+        del path
+        torch.cuda.empty_cache()
+    med = lambda key: float(np.median([p[key] for p in points]))
+    return {"workload": f"layernorm fp16 M={wl.LN_SWEEP_M}, N = 512*i for i = 2..31", "steps_per_point": steps,
+            "median_fwd_frac": round(med("fwd_frac"), 4), "median_bwd_frac": round(med("bwd_frac"), 4),
+            "median_bwd_gbps_page_formula": round(med("bwd_gbps_page_formula"), 1), "points": points}
 
 
 def time_steps(path: Path, steps: int) -> float:
@@ -297,6 +384,9 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": b["bwd_rows"], "kernel_sha": h},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    del path
+    torch.cuda.empty_cache()
+    out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:

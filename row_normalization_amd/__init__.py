@@ -1,7 +1,7 @@
-"""Fused RMSNorm forward/backward for the AMD Instinct MI355X (gfx950).
+"""Fused RMSNorm and LayerNorm forward/backward for the AMD Instinct MI355X (gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of
-``include/rmsnorm.h`` (``librmsnorm.so``, built in-tree by
+``include/rmsnorm.h`` and ``include/layernorm.h`` (``librmsnorm.so``, built in-tree by
 ``row_normalization_amd.build``).  This package only marshals arguments to it;
 there is no CPU or PyTorch fallback.
 """
@@ -9,6 +9,11 @@ from ._lib import (
     LIB_PATH,
     RMSNormError,
     header_functions,
+    layernorm_bwd,
+    layernorm_bwd_rows,
+    layernorm_bwd_workspace_bytes,
+    layernorm_dwdb_reduce,
+    layernorm_fwd,
     lib,
     rmsnorm_bwd,
     rmsnorm_bwd_rows,
@@ -17,7 +22,7 @@ from ._lib import (
     rmsnorm_fwd,
     rmsnorm_status_string,
 )
-from .autograd import CALLS, RMSNorm, RMSNormFunction, rmsnorm
+from .autograd import CALLS, LayerNorm, LayerNormFunction, RMSNorm, RMSNormFunction, layernorm, rmsnorm
 
 __all__ = [
     "LIB_PATH",
@@ -34,4 +39,12 @@ __all__ = [
     "RMSNorm",
     "RMSNormFunction",
     "CALLS",
+    "layernorm_fwd",
+    "layernorm_bwd",
+    "layernorm_bwd_rows",
+    "layernorm_dwdb_reduce",
+    "layernorm_bwd_workspace_bytes",
+    "layernorm",
+    "LayerNorm",
+    "LayerNormFunction",
 ]

@@ -1,4 +1,5 @@
-"""ctypes binding of ``librmsnorm.so`` (the C ABI in ``include/rmsnorm.h``).
+"""ctypes binding of ``librmsnorm.so`` (the C ABI in ``include/rmsnorm.h`` and
+``include/layernorm.h``).
 
 Argument marshalling only: tensors are turned into device pointers, shapes,
 row strides, a dtype code and the current HIP stream, and the C status is
@@ -16,7 +17,8 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librmsnorm.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "rmsnorm.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADERS = (os.path.join(INCLUDE, "rmsnorm.h"), os.path.join(INCLUDE, "layernorm.h"))
 
 F32, BF16, F16 = 0, 1, 2
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -41,6 +43,14 @@ _SIGNATURES = {
     "rmsnorm_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64, _c_i64, _c_i64,
                                    ctypes.c_int, ctypes.c_int, _c_p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "layernorm_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float,
+                                     ctypes.c_int, _c_p]),
+    "layernorm_bwd_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "layernorm_bwd_rows": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64, _c_i64,
+                                          _c_i64, ctypes.c_int, ctypes.POINTER(_c_i64), _c_p]),
+    "layernorm_dwdb_reduce": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "layernorm_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64,
+                                     _c_i64, _c_i64, ctypes.c_int, _c_p]),
 }
 
 _lib = None
@@ -51,10 +61,13 @@ class RMSNormError(RuntimeError):
 
 
 def header_functions() -> list[str]:
-    """Names of the functions ``include/rmsnorm.h`` declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    return re.findall(r"^(?:int|const char\*)\s+(rmsnorm_\w+)\s*\(", text, flags=re.M)
+    """Names of the functions ``include/rmsnorm.h`` and ``include/layernorm.h`` declare."""
+    names = []
+    for h in HEADERS:
+        with open(h) as f:
+            text = f.read()
+        names += re.findall(r"^(?:int|const char\*)\s+((?:rmsnorm|layernorm)_\w+)\s*\(", text, flags=re.M)
+    return names
 
 
 def lib() -> ctypes.CDLL:
@@ -198,3 +211,83 @@ def rmsnorm_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, gemma: bool = False, 
     st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
                            wbytes, M, N, stride, _dtype_code(x), _flags(gemma), _stream(stream))
     _check(st, "rmsnorm_bwd")
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm (include/layernorm.h)
+# ---------------------------------------------------------------------------
+
+def _vec_f32(t, n: int, name: str) -> None:
+    if t.dtype != torch.float32 or t.numel() != n or (n > 1 and t.stride(-1) != 1) or t.dim() != 1:
+        raise ValueError(f"{name} must be a contiguous 1-D float32 tensor of {n} elements")
+
+
+def layernorm_fwd(x, weight, bias, y, mean, rstd, eps: float = 1e-5, stream=None) -> None:
+    """y = (x - mean) * rstd * weight + bias, and the per-row mean and rstd, on the GPU."""
+    _gpu(x, weight, bias, y, mean, rstd)
+    M, N, stride = _rows(x, "x")
+    _same_layout(x, y, "y", stride)
+    for t, name in ((weight, "weight"), (bias, "bias")):
+        if t.dtype != x.dtype or t.numel() != N:
+            raise ValueError(f"{name} must have x's dtype and N elements")
+    _vec_f32(mean, M, "mean")
+    _vec_f32(rstd, M, "rstd")
+    st = lib().layernorm_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), _ptr(mean), _ptr(rstd), M, N, stride,
+                             float(eps), _dtype_code(x), _stream(stream))
+    _check(st, "layernorm_fwd")
+
+
+def layernorm_bwd_workspace_bytes(M: int, N: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DTYPES.get(dtype, -1)
+    out = ctypes.c_size_t(0)
+    _check(lib().layernorm_bwd_workspace_bytes(int(M), int(N), int(code), ctypes.byref(out)),
+           "layernorm_bwd_workspace_bytes")
+    return int(out.value)
+
+
+def _ln_bwd_checks(x, weight, dy, mean, rstd, dx):
+    _gpu(x, weight, dy, mean, rstd, dx)
+    M, N, stride = _rows(x, "x")
+    _same_layout(x, dy, "dy", stride)
+    _same_layout(x, dx, "dx", stride)
+    if weight.dtype != x.dtype or weight.numel() != N:
+        raise ValueError("weight must have x's dtype and N elements")
+    _vec_f32(mean, M, "mean")
+    _vec_f32(rstd, M, "rstd")
+    return M, N, stride
+
+
+def layernorm_bwd_rows(x, weight, dy, mean, rstd, dx, workspace, stream=None) -> int:
+    """dx (may be dy itself) and per-workgroup dw / db partial rows; returns P, the
+    partial-row count (dw partials in rows [0, P), db partials in rows [P, 2P))."""
+    M, N, stride = _ln_bwd_checks(x, weight, dy, mean, rstd, dx)
+    _gpu(workspace)
+    rows = _c_i64(0)
+    st = lib().layernorm_bwd_rows(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), M, N, stride, _dtype_code(x),
+                                  ctypes.byref(rows), _stream(stream))
+    _check(st, "layernorm_bwd_rows")
+    return int(rows.value)
+
+
+def layernorm_dwdb_reduce(partials, rows: int, N: int, dw, db, stream=None) -> None:
+    """dw[j] = sum of partials[p, j] over p < rows; db[j] = sum of partials[rows + p, j]."""
+    _gpu(partials, dw, db)
+    _vec_f32(dw, N, "dw")
+    _vec_f32(db, N, "db")
+    if partials is not None and partials.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    st = lib().layernorm_dwdb_reduce(_ptr(partials), int(rows), int(N), _ptr(dw), _ptr(db), _stream(stream))
+    _check(st, "layernorm_dwdb_reduce")
+
+
+def layernorm_bwd(x, weight, dy, mean, rstd, dx, dw, db, workspace, stream=None) -> None:
+    """Full LayerNorm backward: dx (may be dy itself), dw and db (fp32, overwritten)."""
+    M, N, stride = _ln_bwd_checks(x, weight, dy, mean, rstd, dx)
+    _gpu(dw, db, workspace)
+    _vec_f32(dw, N, "dw")
+    _vec_f32(db, N, "db")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().layernorm_bwd(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dw), _ptr(db),
+                             _ptr(workspace), wbytes, M, N, stride, _dtype_code(x), _stream(stream))
+    _check(st, "layernorm_bwd")

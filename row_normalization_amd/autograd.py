@@ -6,7 +6,11 @@ Autograd và thực sự huấn luyện" (a ``torch.autograd.Function`` whose fo
 saves x, gamma and the inverse RMS for the backward, whose backward returns
 one gradient per forward input, and a call counter that shows the kernel path
 was taken), and the Unsloth walkthrough's ``fast_rms_layernorm`` wrapper
-(section 3; the Gemma weight 1 + gamma).
+(section 3; the Gemma weight 1 + gamma).  The LayerNorm adapter has the
+interface of the LayerNorm chapter (chuoer47.github.io), section 2: a
+``torch.autograd.Function`` called as ``layernorm(x, normalized_shape, weight,
+bias, eps)`` that saves x, weight, bias, mean and rstd and returns
+(dx, None, dw, db, None).
 
 Every computation runs in the HIP kernels (``rmsnorm_fwd``, ``rmsnorm_bwd``);
 this module allocates outputs with torch and marshals arguments.  Inputs of
@@ -19,10 +23,12 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import rmsnorm_bwd, rmsnorm_bwd_workspace_bytes, rmsnorm_fwd
+from ._lib import (layernorm_bwd, layernorm_bwd_workspace_bytes, layernorm_fwd, rmsnorm_bwd,
+                   rmsnorm_bwd_workspace_bytes, rmsnorm_fwd)
 
-# Passes through the adapter (not kernel launches): forward and backward.
-CALLS = {"forward": 0, "backward": 0}
+# Passes through the adapters (not kernel launches): forward and backward,
+# RMSNorm and LayerNorm counted apart.
+CALLS = {"forward": 0, "backward": 0, "ln_forward": 0, "ln_backward": 0}
 
 
 def _rows(t: torch.Tensor) -> torch.Tensor:
@@ -97,3 +103,61 @@ class RMSNorm(torch.nn.Module):
 
     def extra_repr(self) -> str:
         return f"{self.weight.shape[0]}, eps={self.eps}, gemma={self.gemma}"
+
+
+class LayerNormFunction(torch.autograd.Function):
+    """y = (x - mean) * rstd * weight + bias over the last dimension."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, normalized_shape, weight: torch.Tensor, bias: torch.Tensor, eps: float = 1e-5):
+        N = x.shape[-1]
+        if tuple(normalized_shape) != (N,):
+            raise ValueError("normalized_shape must be (x.shape[-1],): LayerNorm over the last dimension only")
+        x2 = _rows(x)
+        y = torch.empty(x2.shape, dtype=x.dtype, device=x.device)
+        mean = torch.empty(x2.shape[0], dtype=torch.float32, device=x.device)
+        rstd = torch.empty(x2.shape[0], dtype=torch.float32, device=x.device)
+        layernorm_fwd(x2, weight, bias, y, mean, rstd, eps=eps)
+        ctx.save_for_backward(x2, weight, bias, mean, rstd)
+        ctx.x_shape = x.shape
+        CALLS["ln_forward"] += 1
+        return y.view(x.shape)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, weight, bias, mean, rstd = ctx.saved_tensors
+        M, N = x2.shape
+        dy2 = dy.reshape(M, N).contiguous()
+        if M > 1 and x2.stride(0) != N:
+            x2 = x2.contiguous()
+        dx = torch.empty_like(dy2)
+        dw = torch.empty(N, dtype=torch.float32, device=dy.device)
+        db = torch.empty(N, dtype=torch.float32, device=dy.device)
+        ws_bytes = layernorm_bwd_workspace_bytes(M, N, x2.dtype)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dy.device)
+        layernorm_bwd(x2, weight, dy2, mean, rstd, dx, dw, db, ws)
+        CALLS["ln_backward"] += 1
+        return dx.view(ctx.x_shape), None, dw.to(weight.dtype), db.to(bias.dtype), None
+
+
+def layernorm(x: torch.Tensor, normalized_shape, weight: torch.Tensor, bias: torch.Tensor,
+              eps: float = 1e-5) -> torch.Tensor:
+    """Functional form with the signature of ``torch.nn.functional.layer_norm``
+    (weight and bias required; normalisation over the last dimension)."""
+    return LayerNormFunction.apply(x, normalized_shape, weight, bias, eps)
+
+
+class LayerNorm(torch.nn.Module):
+    """LayerNorm layer over the last dimension (weight initialised to 1, bias to 0)."""
+
+    def __init__(self, hidden: int, eps: float = 1e-5, dtype=torch.float16, device=None):
+        super().__init__()
+        self.weight = torch.nn.Parameter(torch.ones(hidden, dtype=dtype, device=device))
+        self.bias = torch.nn.Parameter(torch.zeros(hidden, dtype=dtype, device=device))
+        self.eps = eps
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return layernorm(x, (x.shape[-1],), self.weight, self.bias, self.eps)
+
+    def extra_repr(self) -> str:
+        return f"{self.weight.shape[0]}, eps={self.eps}"

@@ -1,8 +1,9 @@
 """Build ``librmsnorm.so`` (gfx950 kernels + host C ABI) in-tree.
 
-``python -m row_normalization_amd.build`` or ``build()``.  The host TU
-(validation, planning, entry points) is compiled by g++, the kernels by hipcc
-for gfx950 only; hipcc links both into one shared library next to this file.
+``python -m row_normalization_amd.build`` or ``build()``.  The host TUs
+(validation, planning, entry points of the RMSNorm and LayerNorm ABIs) are
+compiled by g++, the kernels by hipcc for gfx950 only; hipcc links them into
+one shared library next to this file.  Independent steps run in parallel.
 Packed fp32 vector instructions are disabled in device code.
 """
 from __future__ import annotations
@@ -11,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -37,23 +39,36 @@ def _run(cmd: list[str]) -> None:
         print(out)
 
 
+HOST_SOURCES = ("rmsnorm_api.cpp", "layernorm_api.cpp")
+KERNEL_SOURCES = ("rmsnorm_kernels.hip", "layernorm_kernels.hip")
+
+
 def build(verbose: bool = True) -> str:
     """Compile the library; returns its path.  Always recompiles."""
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     os.makedirs(BUILD, exist_ok=True)
-    api_o = os.path.join(BUILD, "rmsnorm_api.o")
-    ker_o = os.path.join(BUILD, "rmsnorm_kernels.o")
-    tmp = LIB + ".tmp"
-    steps = [
-        ["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
-         f"-I{INCLUDE}", f"-I{os.path.join(ROCM, 'include')}", "-c", os.path.join(CSRC, "rmsnorm_api.cpp"), "-o", api_o],
-        [hipcc, *HIP_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, "rmsnorm_kernels.hip"), "-o", ker_o],
-        [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, ker_o, "-o", tmp],
-    ]
-    for cmd in steps:
+    objects, compile_steps = [], []
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        objects.append(obj)
+        compile_steps.append(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                              f"-I{INCLUDE}", f"-I{os.path.join(ROCM, 'include')}", "-c", os.path.join(CSRC, src),
+                              "-o", obj])
+    for src in KERNEL_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objects.append(obj)
+        compile_steps.append([hipcc, *HIP_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj])
+    for cmd in compile_steps:
         if verbose:
             print("+", " ".join(cmd), flush=True)
-        _run(cmd)
+    with ThreadPoolExecutor(max_workers=len(compile_steps)) as pool:
+        for f in [pool.submit(_run, cmd) for cmd in compile_steps]:
+            f.result()
+    tmp = LIB + ".tmp"
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objects, "-o", tmp]
+    if verbose:
+        print("+", " ".join(link), flush=True)
+    _run(link)
     os.replace(tmp, LIB)
     return LIB
 

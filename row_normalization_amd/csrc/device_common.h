@@ -201,6 +201,26 @@ __device__ __forceinline__ float group_sum(float wave_total, float (*red)[kMaxBl
   return t;
 }
 
+// Two sums per row group (for instance the two row sums of the LayerNorm
+// backward) through one barrier; slots double-buffered by step parity like
+// group_sum.
+__device__ __forceinline__ void group_sum2(float& a, float& b, float (*red)[2][kMaxBlockWaves], int64_t step, int wave,
+                                           int group, int wpr, int lane) {
+  float(*slot)[kMaxBlockWaves] = red[step & 1];
+  if (lane == 0) {
+    slot[0][wave] = a;
+    slot[1][wave] = b;
+  }
+  __syncthreads();
+  float ta = 0.f, tb = 0.f;
+  for (int k = 0; k < wpr; ++k) {
+    ta += slot[0][group * wpr + k];
+    tb += slot[1][group * wpr + k];
+  }
+  a = ta;
+  b = tb;
+}
+
 // Where a lane sits: its wave (uniform, in a scalar register), the row group
 // of the wave and the wave within the group.
 struct Lane {
@@ -221,6 +241,24 @@ struct Lane {
 __device__ __forceinline__ int64_t row_of(int64_t step, int64_t row_iters, int rpb, int group) {
   (void)row_iters;
   return (step * gridDim.x + blockIdx.x) * rpb + group;
+}
+
+// Host-side dispatch from a plan's vectors-per-lane count to the compiled
+// instantiation (one launcher per entry of kItersSet).
+template <typename Args, hipError_t (*L1)(const RowPlan&, const Args&, hipStream_t),
+          hipError_t (*L2)(const RowPlan&, const Args&, hipStream_t), hipError_t (*L4)(const RowPlan&, const Args&, hipStream_t),
+          hipError_t (*L5)(const RowPlan&, const Args&, hipStream_t), hipError_t (*L8)(const RowPlan&, const Args&, hipStream_t),
+          hipError_t (*L16)(const RowPlan&, const Args&, hipStream_t)>
+hipError_t pick_iters(const RowPlan& p, const Args& a, hipStream_t s) {
+  switch (p.iters) {
+    case 1: return L1(p, a, s);
+    case 2: return L2(p, a, s);
+    case 4: return L4(p, a, s);
+    case 5: return L5(p, a, s);
+    case 8: return L8(p, a, s);
+    case 16: return L16(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dev

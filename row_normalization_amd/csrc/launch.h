@@ -1,6 +1,7 @@
-// Internal interface between the host-side C ABI (rmsnorm_api.cpp: argument
-// validation and launch planning, no device code) and the gfx950 kernels
-// (rmsnorm_kernels.hip).  Not installed, not part of the ABI.
+// Internal interface between the host-side C ABIs (rmsnorm_api.cpp and
+// layernorm_api.cpp: argument validation and launch planning, no device code)
+// and the gfx950 kernels (rmsnorm_kernels.hip, layernorm_kernels.hip).  Not
+// installed, not part of the ABI.
 #pragma once
 
 #include <stdint.h>
@@ -64,16 +65,80 @@ struct BwdArgs {
   int64_t row_iters;
 };
 
+// Column sums of one or two [rows, N] fp32 tables stored back to back
+// (table t starts at partials + t * rows * N and is summed into dgamma for
+// t = 0, into dgamma2 for t = 1).
 struct ReduceArgs {
   const float* partials;
   float* dgamma;
   int64_t rows;
   int32_t N;
+  float* dgamma2;  // null for one table
+};
+
+// LayerNorm forward: y = (x - mean) * rstd * weight + bias, mean and rstd per row.
+struct LnFwdArgs {
+  const void* x;
+  const void* weight;
+  const void* bias;
+  void* y;
+  float* mean;
+  float* rstd;
+  int64_t M;
+  int64_t stride;
+  int32_t N;
+  int32_t nvec;
+  float eps;
+  float inv_n;
+  int32_t wpr;
+  int32_t rpb;
+  int64_t row_iters;
+};
+
+// LayerNorm backward row pass: dx, and per-workgroup partial rows of dw
+// (partials[0 .. grid)) and db (partials[grid .. 2 grid)).
+struct LnBwdArgs {
+  const void* x;
+  const void* weight;
+  const void* dy;
+  const float* mean;
+  const float* rstd;
+  void* dx;  // may equal dy
+  float* partials;  // [2, grid, N] fp32
+  int64_t M;
+  int64_t stride;
+  int32_t N;
+  int32_t nvec;
+  float inv_n;
+  int32_t wpr;
+  int32_t rpb;
+  int64_t row_iters;
 };
 
 // Compiled-in register-array lengths for the row kernels.
 constexpr int kItersSet[] = {1, 2, 4, 5, 8, 16};
 constexpr int kItersMax = 16;
+
+// Register model of the row kernels: the elements of a row one lane may own
+// (vec * iters at most) so that its row data fits in kLaneDataRegs 32-bit
+// registers (of the 128 a lane of a 1024-thread workgroup may use).  Costs
+// per element, in quarter registers: a packed operand costs its element size,
+// an fp32 value 4.
+//   RMSNorm forward   x and gamma packed
+//   RMSNorm backward  x and dy packed; fp32 weight and dgamma partial
+//   LayerNorm forward x, weight and bias packed, plus a quarter register per
+//                     element for the conversions of three operands (at 64
+//                     fp16 elements per lane the compiler spills otherwise)
+//   LayerNorm backward x and dy packed; fp32 weight, dw and db partials
+// The host planner never picks more; the dispatch compiles nothing beyond it.
+constexpr int kLaneDataRegs = 96;
+enum class RowOp { kRmsFwd, kRmsBwd, kLnFwd, kLnBwd };
+constexpr int lane_elems_cap(RowOp op, int elsize) {
+  return kLaneDataRegs * 4 / (op == RowOp::kRmsFwd   ? 2 * elsize
+                              : op == RowOp::kRmsBwd ? 2 * elsize + 8
+                              : op == RowOp::kLnFwd  ? 3 * elsize + 1
+                                                     : 2 * elsize + 12);
+}
 
 // Tile of the dgamma reduction: kReduceCols column threads (a 128-byte row
 // segment with 16-byte loads) x kReduceSlices row slices per 256-thread block.
@@ -83,6 +148,9 @@ constexpr int kReduceSlices = 32;
 // dtype codes match rmsnorm_dtype (0 fp32, 1 bf16, 2 fp16).  Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(int dtype, const RowPlan& p, const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStream_t s);
-hipError_t launch_dgamma_reduce(int vec, const ReduceArgs& a, hipStream_t s);
+// `tables` is 1 (dgamma) or 2 (dgamma and dgamma2).
+hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t s);
+hipError_t launch_ln_fwd(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s);
+hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t s);
 
 }  // namespace rmsn

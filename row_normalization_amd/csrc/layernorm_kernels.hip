@@ -1,0 +1,355 @@
+// gfx950 (CDNA4) kernels for fused LayerNorm forward and backward.
+//
+// What is computed (the LayerNorm chapter "第 07 章:LayerNorm——反向传播与原子锁"
+// of a Triton tutorial series, chuoer47.github.io; section 1 for the forward,
+// sections 3.0 and 3.3 for the input gradient, 3.3-3.5 for the weight and
+// bias gradients):
+//   forward   mean = sum(x)/N, var = sum((x - mean)^2)/N, rstd = 1/sqrt(var + eps),
+//             y = (x - mean) * rstd * w + b
+//   backward  x_hat = (x - mean) * rstd, g = w * dy, c1 = sum(x_hat * g)/N,
+//             c2 = sum(g)/N, dx = (g - (x_hat * c1 + c2)) * rstd,
+//             dw = sum_rows dy * x_hat, db = sum_rows dy
+//
+// The kernels share the RMSNorm kernels' skeleton (device_common.h): whole
+// 16-byte column vectors per lane, every row access an unconditional raw
+// buffer operation through a per-row descriptor (the hardware range check
+// masks the tail and the rows past M), nontemporal streaming of x, dy, y and
+// dx, DPP wave sums and one LDS barrier per cross-wave sum.
+//  - The forward keeps the row in registers and takes the page's two passes
+//    over it there: the mean first, then the sum of squared differences from
+//    it (no E[x^2] - mean^2 cancellation), so x is read from HBM once.  The
+//    second pass masks the vectors past N, whose zeros would otherwise add
+//    mean^2 each.
+//  - The backward needs two row sums, c1 and c2; they travel together through
+//    one barrier.  Past-the-end vectors need no mask there: their dy and w
+//    read as zero, so they add nothing to either sum or to the gradients.
+//  - Instead of the page's lock-protected accumulation into GROUP_SIZE
+//    intermediate rows, the backward is a persistent grid: each workgroup
+//    keeps its dw and db column partials in fp32 registers across its rows
+//    and writes one partial row of each; the RMSNorm column-sum kernel then
+//    adds the partial rows in a fixed order (both tables in one launch).  No
+//    locks, no atomics: every result is bitwise reproducible.
+//  - dx may be written over dy (each lane loads its dy elements before it
+//    stores the same elements of dx).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace rmsn {
+namespace {
+using namespace dev;
+
+// Streamed operands are touched once per pass: nontemporal, as for RMSNorm.
+constexpr int kLnLoadX = kNontemporal;
+constexpr int kLnStoreY = kNontemporal;
+constexpr int kLnLoadXdy = kNontemporal;
+constexpr int kLnStoreDx = kNontemporal;
+
+// ---------------------------------------------------------------------------
+// Forward.  Not persistent: the grid covers the row groups (capped, then
+// looped).  weight and bias come from the caches for every row.
+// ---------------------------------------------------------------------------
+template <typename S, int VEC, int ITERS>
+__global__ __launch_bounds__(1024) void layernorm_fwd_kernel(const LnFwdArgs a) {
+  constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  const Lane L(a.wpr);
+  __shared__ float red[2][kMaxBlockWaves];
+
+  const uint32_t voff = L.first_vec() * kPack;
+  const uint32_t iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  const Rsrc rw = make_rsrc(a.weight, row_bytes);
+  const Rsrc rb = make_rsrc(a.bias, row_bytes);
+  const Rsrc rmean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
+  const Rsrc rrstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+  const S* x = static_cast<const S*>(a.x);
+  S* y = static_cast<S*>(a.y);
+
+  for (int64_t step = 0; step < a.row_iters; ++step) {
+    const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
+    const bool active = row < a.M;
+    const int64_t off = active ? row * a.stride : 0;
+    const Rsrc rx = make_rsrc(x + off, active ? row_bytes : 0u);
+    const Rsrc ry = make_rsrc(y + off, active ? row_bytes : 0u);
+
+    Pack<S, VEC> xv[ITERS];
+    Pack<S, VEC> wv[ITERS];
+    Pack<S, VEC> bv[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) xv[i] = buf_load<S, VEC, kLnLoadX>(rx, voff + i * iter_bytes);
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) wv[i] = buf_load<S, VEC, kDefault>(rw, voff + i * iter_bytes);
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) bv[i] = buf_load<S, VEC, kDefault>(rb, voff + i * iter_bytes);
+
+    // pass 1: the mean (vectors past N read as zero and add nothing)
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s += xv[i].get(e);
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) xv[i].keep_packed();
+    s = wave_sum(s);
+    if (a.wpr > 1) s = group_sum(s, red, 2 * step, L.wave, L.group, a.wpr, L.lane);
+    const float mean = s * a.inv_n;
+
+    // pass 2: squared differences from the mean, over the columns < N only
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const bool in_row = static_cast<int>((i * a.wpr + L.wv) * kWave + L.lane) < a.nvec;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float t = in_row ? xv[i].get(e) - mean : 0.f;
+        d = fmaf(t, t, d);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) xv[i].keep_packed();
+    d = wave_sum(d);
+    if (a.wpr > 1) d = group_sum(d, red, 2 * step + 1, L.wave, L.group, a.wpr, L.lane);
+    const float rstd = rsqrtf(fmaf(d, a.inv_n, a.eps));
+
+    // one lane per row writes mean and rstd; the others' offsets are out of range
+    const bool writer = active && L.wv == 0 && L.lane == 0;
+    const uint32_t soff = writer ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mean), rmean, soff, 0, kDefault);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, rstd), rrstd, soff, 0, kDefault);
+
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = fmaf((xv[i].get(e) - mean) * rstd, wv[i].get(e), bv[i].get(e));
+      buf_store<S, VEC, kLnStoreY>(round_pack<S, VEC>(o), ry, voff + i * iter_bytes);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward row pass: dx, and per-workgroup partial rows of dw and db.
+// Persistent: workgroup b takes rows (k * grid + b) * rpb + group.  A lane
+// keeps, for the columns it owns, w in fp32 and its dw and db partials in
+// fp32 registers across all of its rows.
+// ---------------------------------------------------------------------------
+template <typename S, int VEC, int ITERS>
+__global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float comb[];  // 2N floats, when rpb > 1
+  __shared__ float red[2][2][kMaxBlockWaves];
+  constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  const Lane L(a.wpr);
+  const uint32_t voff = L.first_vec() * kPack;
+  const uint32_t iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  const Rsrc rmean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
+  const Rsrc rrstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+
+  float w[ITERS][VEC];
+  float accw[ITERS][VEC];
+  float accb[ITERS][VEC];
+  {
+    const Rsrc rw = make_rsrc(a.weight, row_bytes);
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const Pack<S, VEC> g = buf_load<S, VEC, kDefault>(rw, voff + i * iter_bytes);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        w[i][e] = g.get(e);
+        accw[i][e] = 0.f;
+        accb[i][e] = 0.f;
+      }
+    }
+  }
+
+  for (int64_t step = 0; step < a.row_iters; ++step) {
+    const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
+    const bool active = row < a.M;
+    const int64_t off = active ? row * a.stride : 0;
+    const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? row_bytes : 0u);
+    const Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + off, active ? row_bytes : 0u);
+    const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + off, active ? row_bytes : 0u);
+
+    Pack<S, VEC> xv[ITERS];
+    Pack<S, VEC> dv[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      xv[i] = buf_load<S, VEC, kLnLoadXdy>(rx, voff + i * iter_bytes);
+      dv[i] = buf_load<S, VEC, kLnLoadXdy>(rd, voff + i * iter_bytes);
+    }
+    // mean and rstd of a missing row read as zero (out of the descriptors' range)
+    const uint32_t soff = active ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+    const float mean = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rmean, soff, 0, kDefault));
+    const float rstd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrstd, soff, 0, kDefault));
+
+    // the two row sums: of x_hat * g and of g, with g = w * dy
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float xh = (xv[i].get(e) - mean) * rstd;
+        const float g = w[i][e] * dv[i].get(e);
+        s1 = fmaf(xh, g, s1);
+        s2 += g;
+      }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      xv[i].keep_packed();
+      dv[i].keep_packed();
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (a.wpr > 1) group_sum2(s1, s2, red, step, L.wave, L.group, a.wpr, L.lane);
+    const float c1 = s1 * a.inv_n;
+    const float c2 = s2 * a.inv_n;
+
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float df = dv[i].get(e);
+        const float xh = (xv[i].get(e) - mean) * rstd;
+        o[e] = (w[i][e] * df - fmaf(xh, c1, c2)) * rstd;
+        accw[i][e] = fmaf(df, xh, accw[i][e]);
+        accb[i][e] += df;
+      }
+      buf_store<S, VEC, kLnStoreDx>(round_pack<S, VEC>(o), rdx, voff + i * iter_bytes);
+    }
+  }
+
+  // One dw and one db partial row per workgroup; row groups are added in LDS
+  // in group order.
+  float* pw = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
+  float* pb = a.partials + (static_cast<int64_t>(gridDim.x) + blockIdx.x) * a.N;
+  if (a.rpb == 1) {
+    const Rsrc rdw = make_rsrc(pw, static_cast<uint32_t>(a.N) * 4u);
+    const Rsrc rdb = make_rsrc(pb, static_cast<uint32_t>(a.N) * 4u);
+    const uint32_t voff32 = L.first_vec() * VEC * 4u;
+    const uint32_t iter32 = static_cast<uint32_t>(a.wpr) * kWave * VEC * 4u;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      buf_store_f32<VEC, kDefault>(accw[i], rdw, voff32 + i * iter32);
+      buf_store_f32<VEC, kDefault>(accb[i], rdb, voff32 + i * iter32);
+    }
+    return;
+  }
+  for (int g = 0; g < a.rpb; ++g) {
+    __syncthreads();
+    if (L.group == g) {
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) {
+        const int v = (i * a.wpr + L.wv) * kWave + L.lane;
+        if (v < a.nvec) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            float* cw = comb + v * VEC + e;
+            float* cb = cw + a.N;
+            *cw = (g == 0) ? accw[i][e] : *cw + accw[i][e];
+            *cb = (g == 0) ? accb[i][e] : *cb + accb[i][e];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int col = threadIdx.x; col < a.N; col += blockDim.x) {
+    pw[col] = comb[col];
+    pb[col] = comb[a.N + col];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch to the compiled instantiations.
+// ---------------------------------------------------------------------------
+template <typename S, int VEC, int ITERS>
+hipError_t ln_fwd_inst(const RowPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  if constexpr (VEC * ITERS > lane_elems_cap(RowOp::kLnFwd, sizeof(S))) {
+    return hipErrorInvalidValue;  // beyond the register model: never planned, not compiled
+  } else {
+    hipLaunchKernelGGL((layernorm_fwd_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)), dim3(p.threads()), 0,
+                       s, a);
+    return hipGetLastError();
+  }
+}
+
+template <typename S, int VEC, int ITERS>
+hipError_t ln_bwd_inst(const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
+  if constexpr (VEC * ITERS > lane_elems_cap(RowOp::kLnBwd, sizeof(S))) {
+    return hipErrorInvalidValue;  // beyond the register model: never planned, not compiled
+  } else {
+    const size_t lds = p.rpb > 1 ? 2 * static_cast<size_t>(a.N) * sizeof(float) : 0;
+    hipLaunchKernelGGL((layernorm_bwd_rows_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)),
+                       dim3(p.threads()), lds, s, a);
+    return hipGetLastError();
+  }
+}
+
+template <typename S, int VEC>
+hipError_t ln_fwd_vec(const RowPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  return pick_iters<LnFwdArgs, ln_fwd_inst<S, VEC, 1>, ln_fwd_inst<S, VEC, 2>, ln_fwd_inst<S, VEC, 4>,
+                    ln_fwd_inst<S, VEC, 5>, ln_fwd_inst<S, VEC, 8>, ln_fwd_inst<S, VEC, 16>>(p, a, s);
+}
+
+template <typename S, int VEC>
+hipError_t ln_bwd_vec(const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
+  return pick_iters<LnBwdArgs, ln_bwd_inst<S, VEC, 1>, ln_bwd_inst<S, VEC, 2>, ln_bwd_inst<S, VEC, 4>,
+                    ln_bwd_inst<S, VEC, 5>, ln_bwd_inst<S, VEC, 8>, ln_bwd_inst<S, VEC, 16>>(p, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_ln_fwd(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  if (dtype == 0) {
+    switch (p.vec) {
+      case 1: return ln_fwd_vec<float, 1>(p, a, s);
+      case 2: return ln_fwd_vec<float, 2>(p, a, s);
+      case 4: return ln_fwd_vec<float, 4>(p, a, s);
+    }
+  } else if (dtype == 1) {
+    switch (p.vec) {
+      case 1: return ln_fwd_vec<uint16_t, 1>(p, a, s);
+      case 2: return ln_fwd_vec<uint16_t, 2>(p, a, s);
+      case 4: return ln_fwd_vec<uint16_t, 4>(p, a, s);
+      case 8: return ln_fwd_vec<uint16_t, 8>(p, a, s);
+    }
+  } else if (dtype == 2) {
+    switch (p.vec) {
+      case 1: return ln_fwd_vec<_Float16, 1>(p, a, s);
+      case 2: return ln_fwd_vec<_Float16, 2>(p, a, s);
+      case 4: return ln_fwd_vec<_Float16, 4>(p, a, s);
+      case 8: return ln_fwd_vec<_Float16, 8>(p, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
+  if (dtype == 0) {
+    switch (p.vec) {
+      case 1: return ln_bwd_vec<float, 1>(p, a, s);
+      case 2: return ln_bwd_vec<float, 2>(p, a, s);
+      case 4: return ln_bwd_vec<float, 4>(p, a, s);
+    }
+  } else if (dtype == 1) {
+    switch (p.vec) {
+      case 1: return ln_bwd_vec<uint16_t, 1>(p, a, s);
+      case 2: return ln_bwd_vec<uint16_t, 2>(p, a, s);
+      case 4: return ln_bwd_vec<uint16_t, 4>(p, a, s);
+      case 8: return ln_bwd_vec<uint16_t, 8>(p, a, s);
+    }
+  } else if (dtype == 2) {
+    switch (p.vec) {
+      case 1: return ln_bwd_vec<_Float16, 1>(p, a, s);
+      case 2: return ln_bwd_vec<_Float16, 2>(p, a, s);
+      case 4: return ln_bwd_vec<_Float16, 4>(p, a, s);
+      case 8: return ln_bwd_vec<_Float16, 8>(p, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rmsn

@@ -10,136 +10,17 @@
 #include <initializer_list>
 #include <limits>
 
+#include "host_plan.h"
 #include "launch.h"
 
 namespace rmsn {
 namespace {
 
-// Launch shape.  A row group spans as many waves as it takes for each lane
-// to hold kLaneVectors 16-byte vectors of every row operand; workgroups hold
-// about kBlockWaves waves (several row groups when rows are short).  Measured
-// on MI355X at M=16384, N=8192 bf16: two vectors per lane and eight waves per
-// row beat both fewer, fatter lanes and whole-row-per-wave layouts, for the
-// forward and the backward alike.
-constexpr int kLaneVectors = 2;
-constexpr int kBlockWaves = 8;
-constexpr int kFwdRowWaves = 8;
-// The backward grid is persistent: a whole number of workgroups on each of
-// the 256 compute units (a power of two, so that every CU gets the same
-// count), about kBwdResidentWaves waves per CU, every workgroup taking a fixed
-// share of the rows.  Each workgroup writes one fp32 partial row of dgamma.
-// (A grid that does not divide evenly over the CUs leaves a tail: 819
-// workgroups for N = 5120 ran 20 % slower than 512.)
-constexpr int64_t kComputeUnits = 256;
-constexpr int64_t kBwdResidentWaves = 16;
-// Upper bound on the backward grid, hence on the partial rows a workspace
-// must hold (rmsnorm_bwd_workspace_bytes promises this many rows at most).
-constexpr int64_t kBwdGridMax = 1024;
-// The forward grid is not persistent; it is only capped so that the grid
-// dimension stays small (rows beyond it are taken in further steps).
-constexpr int64_t kFwdGridMax = 1 << 20;
-// Register budget per lane for the row data, in 32-bit registers (of the 128
-// a lane of a 1024-thread workgroup may use): the forward holds x and gamma
-// packed; the backward holds x and dy packed plus, per column it owns, the
-// fp32 weight and dgamma partial.
-constexpr int kLaneDataRegs = 96;
-
-int elsize(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-bool aligned(const void* p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(bytes) == 0; }
-
-// [p, p + len) for a byte range; empty ranges never overlap.
-struct Span {
-  uintptr_t lo;
-  uintptr_t len;
-};
-Span span(const void* p, int64_t bytes) { return {reinterpret_cast<uintptr_t>(p), static_cast<uintptr_t>(bytes)}; }
-bool overlap(Span a, Span b) { return a.len && b.len && a.lo < b.lo + b.len && b.lo < a.lo + a.len; }
-
-int64_t matrix_bytes(int64_t M, int64_t N, int64_t stride, int dtype) {
-  return M == 0 ? 0 : ((M - 1) * stride + N) * elsize(dtype);
-}
-
 int check_common(int64_t M, int64_t N, int64_t stride, int dtype, int flags) {
   if (dtype != RMSNORM_F32 && dtype != RMSNORM_BF16 && dtype != RMSNORM_F16) return RMSNORM_E_DTYPE;
   if (flags & ~(RMSNORM_GEMMA | RMSNORM_ROUND_NORMED)) return RMSNORM_E_FLAG;
-  if (M < 0 || M > RMSNORM_M_MAX || N < 1 || N > RMSNORM_N_MAX) return RMSNORM_E_SHAPE;
-  if (stride < N) return RMSNORM_E_STRIDE;
-  // element offsets must stay well inside int64 even for the last row
-  if (M > 0 && stride > (std::numeric_limits<int64_t>::max() / 8) / M) return RMSNORM_E_SHAPE;
-  return RMSNORM_OK;
+  return check_shape(M, N, stride);
 }
-
-// Widest vector (up to 16 bytes) that every pointer, N and the stride allow.
-int choose_vec(int dtype, int64_t N, int64_t stride, std::initializer_list<const void*> ptrs) {
-  const int es = elsize(dtype);
-  for (int vec = 16 / es; vec > 1; vec /= 2) {
-    bool ok = N % vec == 0 && stride % vec == 0;
-    for (const void* p : ptrs) ok = ok && aligned(p, int64_t(vec) * es);
-    if (ok) return vec;
-  }
-  return 1;
-}
-
-// Waves per row and vectors per lane: among 1..16 waves per row and the
-// compiled register-array lengths, the shape that wastes the fewest lanes;
-// ties go to the length nearest `target` vectors per lane, then to fewer waves.
-bool row_shape(int64_t nvec, int iters_cap, int target, int* wpr, int* iters) {
-  int64_t best_waste = -1;
-  int best_dist = 0;
-  for (int w = 1; w <= kMaxBlockWaves; ++w) {
-    for (int it : kItersSet) {
-      if (it > iters_cap || int64_t(it) * kWave * w < nvec) continue;
-      const int64_t waste = int64_t(it) * kWave * w - nvec;
-      const int dist = it > target ? it - target : target - it;
-      if (best_waste < 0 || waste < best_waste || (waste == best_waste && dist < best_dist)) {
-        best_waste = waste;
-        best_dist = dist;
-        *wpr = w;
-        *iters = it;
-      }
-    }
-  }
-  return best_waste >= 0;
-}
-
-// Elements per lane the register budget allows.
-int lane_elems_cap(int dtype, bool backward) {
-  const int es = elsize(dtype);
-  // registers per element, in quarters: packed operands (es each), fp32 values (4 each)
-  return backward ? kLaneDataRegs * 4 / (2 * es + 8) : kLaneDataRegs * 4 / (2 * es);
-}
-
-RowPlan plan_rows(int64_t M, int64_t N, int vec, int dtype, bool backward) {
-  RowPlan p{};
-  p.vec = vec;
-  const int64_t nvec = N / vec;
-  const int cap = std::min(kItersMax, std::max(1, lane_elems_cap(dtype, backward) / vec));
-  // The forward prefers rows of at most kFwdRowWaves waves, with more vectors
-  // per lane beyond that (measured at N = 16384 bf16: 8 waves x 4 vectors ran
-  // 4 % faster than 16 x 2); the backward keeps kLaneVectors.
-  const int target =
-      backward ? kLaneVectors : static_cast<int>(std::max<int64_t>(kLaneVectors, ceil_div(nvec, int64_t(kWave) * kFwdRowWaves)));
-  if (!row_shape(nvec, cap, target, &p.wpr, &p.iters)) {
-    p.iters = 0;  // cannot happen for N <= RMSNORM_N_MAX
-    return p;
-  }
-  p.rpb = std::max(1, kBlockWaves / p.wpr);
-  const int64_t groups = ceil_div(M, p.rpb);
-  int64_t per_cu = 1;
-  while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
-  const int64_t grid_cap = backward ? std::min(kBwdGridMax, kComputeUnits * per_cu) : kFwdGridMax;
-  p.grid = std::max<int64_t>(1, std::min(groups, grid_cap));
-  p.row_iters = ceil_div(groups, p.grid);
-  return p;
-}
-
-int64_t partial_rows_bound(int64_t M) { return std::min(M, kBwdGridMax); }
-
-int hip_status(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_E_HIP; }
-
 // Validation shared by rmsnorm_bwd_rows and rmsnorm_bwd.  `dgamma` is null
 // for the row pass alone.
 int check_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, const void* dx, const float* dgamma,
@@ -177,7 +58,7 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
                             void* workspace, int64_t M, int64_t N, int64_t stride, int dtype, int flags,
                             int64_t* rows_written, hipStream_t stream) {
   const int vec = choose_vec(dtype, N, stride, {x, gamma, dy, dx});
-  const RowPlan p = plan_rows(M, N, vec, dtype, true);
+  const RowPlan p = plan_rows(M, N, vec, lane_elems_cap(RowOp::kRmsBwd, elsize(dtype)), true);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   BwdArgs a{};
   a.x = x;
@@ -202,8 +83,8 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
 
 int launch_reduce_checked(const float* partials, int64_t rows, int64_t N, float* dgamma, hipStream_t stream) {
   const int vec = (N % 4 == 0 && aligned(dgamma, 16) && (rows == 0 || aligned(partials, 16))) ? 4 : 1;
-  ReduceArgs a{partials, dgamma, rows, static_cast<int32_t>(N)};
-  return hip_status(launch_dgamma_reduce(vec, a, stream));
+  ReduceArgs a{partials, dgamma, rows, static_cast<int32_t>(N), nullptr};
+  return hip_status(launch_dgamma_reduce(vec, 1, a, stream));
 }
 
 }  // namespace
@@ -228,7 +109,7 @@ int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t 
     return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, gamma, y});
-  const RowPlan p = plan_rows(M, N, vec, dtype, false);
+  const RowPlan p = plan_rows(M, N, vec, lane_elems_cap(RowOp::kRmsFwd, elsize(dtype)), false);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   FwdArgs a{};
   a.x = x;

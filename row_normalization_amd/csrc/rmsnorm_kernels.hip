@@ -286,6 +286,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
 // slices; slice s sums rows s, s + slices, ...; the slices are then added in
 // slice order.  Loads go through a descriptor over the whole partials table,
 // so rows past the end read as zero and every load is unconditional.
+// blockIdx.y picks the table when two are reduced in one launch (the
+// LayerNorm weight and bias gradients).
 // ---------------------------------------------------------------------------
 template <int VEC>
 __global__ __launch_bounds__(kReduceCols * kReduceSlices) void rmsnorm_dgamma_reduce_kernel(const ReduceArgs a) {
@@ -294,7 +296,9 @@ __global__ __launch_bounds__(kReduceCols * kReduceSlices) void rmsnorm_dgamma_re
   const int tc = threadIdx.x % kReduceCols;
   const int ts = threadIdx.x / kReduceCols;
   const int col = (blockIdx.x * kReduceCols + tc) * VEC;
-  const Rsrc rp = make_rsrc(a.partials, static_cast<uint32_t>(a.rows * a.N) * 4u);
+  const float* table = a.partials + static_cast<int64_t>(blockIdx.y) * a.rows * a.N;
+  float* out = blockIdx.y ? a.dgamma2 : a.dgamma;
+  const Rsrc rp = make_rsrc(table, static_cast<uint32_t>(a.rows * a.N) * 4u);
   const uint32_t slice_bytes = static_cast<uint32_t>(kReduceSlices) * static_cast<uint32_t>(a.N) * 4u;
   const uint32_t voff = (static_cast<uint32_t>(ts) * static_cast<uint32_t>(a.N) + static_cast<uint32_t>(col)) * 4u;
   float acc[VEC];
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kReduceCols * kReduceSlices) void rmsnorm_dgamma_re
       for (int s = 1; s < kReduceSlices; ++s) t += part[s][tc * VEC + e];
       o[e] = t;
     }
-    *reinterpret_cast<Pack<float, VEC>*>(a.dgamma + col) = round_pack<float, VEC>(o);
+    *reinterpret_cast<Pack<float, VEC>*>(out + col) = round_pack<float, VEC>(o);
   }
 }
 
@@ -331,32 +335,24 @@ __global__ __launch_bounds__(kReduceCols * kReduceSlices) void rmsnorm_dgamma_re
 // ---------------------------------------------------------------------------
 template <typename S, int VEC, int ITERS>
 hipError_t fwd_inst(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rmsnorm_fwd_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)), dim3(p.threads()), 0, s,
-                     a);
-  return hipGetLastError();
+  if constexpr (VEC * ITERS > lane_elems_cap(RowOp::kRmsFwd, sizeof(S))) {
+    return hipErrorInvalidValue;  // beyond the register model: never planned, not compiled
+  } else {
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)), dim3(p.threads()), 0, s,
+                       a);
+    return hipGetLastError();
+  }
 }
 
 template <typename S, int VEC, int ITERS>
 hipError_t bwd_inst(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-  const size_t lds = p.rpb > 1 ? static_cast<size_t>(a.N) * sizeof(float) : 0;
-  hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)),
-                     dim3(p.threads()), lds, s, a);
-  return hipGetLastError();
-}
-
-template <typename Args, hipError_t (*L1)(const RowPlan&, const Args&, hipStream_t),
-          hipError_t (*L2)(const RowPlan&, const Args&, hipStream_t), hipError_t (*L4)(const RowPlan&, const Args&, hipStream_t),
-          hipError_t (*L5)(const RowPlan&, const Args&, hipStream_t), hipError_t (*L8)(const RowPlan&, const Args&, hipStream_t),
-          hipError_t (*L16)(const RowPlan&, const Args&, hipStream_t)>
-hipError_t pick_iters(const RowPlan& p, const Args& a, hipStream_t s) {
-  switch (p.iters) {
-    case 1: return L1(p, a, s);
-    case 2: return L2(p, a, s);
-    case 4: return L4(p, a, s);
-    case 5: return L5(p, a, s);
-    case 8: return L8(p, a, s);
-    case 16: return L16(p, a, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (VEC * ITERS > lane_elems_cap(RowOp::kRmsBwd, sizeof(S))) {
+    return hipErrorInvalidValue;  // beyond the register model: never planned, not compiled
+  } else {
+    const size_t lds = p.rpb > 1 ? static_cast<size_t>(a.N) * sizeof(float) : 0;
+    hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)),
+                       dim3(p.threads()), lds, s, a);
+    return hipGetLastError();
   }
 }
 
@@ -424,13 +420,14 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_dgamma_reduce(int vec, const ReduceArgs& a, hipStream_t s) {
+hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t s) {
   const int cols = kReduceCols * vec;
-  const unsigned grid = static_cast<unsigned>((a.N + cols - 1) / cols);
+  const dim3 grid(static_cast<unsigned>((a.N + cols - 1) / cols), static_cast<unsigned>(tables));
+  if (tables != 1 && tables != 2) return hipErrorInvalidValue;
   if (vec == 4) {
-    hipLaunchKernelGGL(rmsnorm_dgamma_reduce_kernel<4>, dim3(grid), dim3(kReduceCols * kReduceSlices), 0, s, a);
+    hipLaunchKernelGGL(rmsnorm_dgamma_reduce_kernel<4>, grid, dim3(kReduceCols * kReduceSlices), 0, s, a);
   } else if (vec == 1) {
-    hipLaunchKernelGGL(rmsnorm_dgamma_reduce_kernel<1>, dim3(grid), dim3(kReduceCols * kReduceSlices), 0, s, a);
+    hipLaunchKernelGGL(rmsnorm_dgamma_reduce_kernel<1>, grid, dim3(kReduceCols * kReduceSlices), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
