@@ -11,11 +11,13 @@ import types
 
 import pytest
 
-from tests import oracle_pins, oracle_pins_ln
+from tests import oracle_pins, oracle_pins_ln, oracle_pins_rope, oracle_pins_swiglu
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE_DIR, "rmsnorm_oracle.py")
 LN_SRC = os.path.join(ORACLE_DIR, "layernorm_oracle.py")
+ROPE_SRC = os.path.join(ORACLE_DIR, "rope_oracle.py")
+SWIGLU_SRC = os.path.join(ORACLE_DIR, "swiglu_oracle.py")
 
 MUTANTS = {
     "denominator_n_plus_1": ("mean_sq = np.sum(x * x, axis=1) / n", "mean_sq = np.sum(x * x, axis=1) / (n + 1)"),
@@ -120,3 +122,69 @@ def test_layernorm_mutant_is_caught(name):
         except Exception as e:
             caught.append((pin.__name__, type(e).__name__))
     assert caught, f"no pin rejects the LayerNorm mutant {name!r}"
+
+
+ROPE_MUTANTS = {
+    "rope_first_sign": ("q1 * c - q2 * s", "q1 * c + q2 * s"),
+    "rope_second_sign": ("q2 * c + q1 * s", "q2 * c - q1 * s"),
+    "rope_interleaved_pairs": ("    q1 = q[..., :half]\n    q2 = q[..., half:]", "    q1 = q[..., ::2]\n    q2 = q[..., 1::2]"),
+    "rope_halves_swapped": ("    q1 = q[..., :half]\n    q2 = q[..., half:]", "    q1 = q[..., half:]\n    q2 = q[..., :half]"),
+    "rope_cos_sin_swapped": ("c = np.asarray(cos, dtype=np.float64)[pos]", "c = np.asarray(sin, dtype=np.float64)[pos]"),
+    "rope_backward_same_sin": ("return rotate(dq, cos, -np.asarray(sin, dtype=np.float64), pos)",
+                               "return rotate(dq, cos, np.asarray(sin, dtype=np.float64), pos)"),
+    "rope_backward_negates_cos": ("return rotate(dq, cos, -np.asarray(sin, dtype=np.float64), pos)",
+                                  "return rotate(dq, -np.asarray(cos, dtype=np.float64), sin, pos)"),
+    "rope_positions_offset": ("% seq_len", "% seq_len + 1"),
+    "rope_positions_ignored": ("return np.asarray(positions, dtype=np.int64)", "return np.arange(n_tokens) % seq_len"),
+    "rope_output_halves_swapped": ("np.concatenate([q1 * c - q2 * s, q2 * c + q1 * s], axis=-1)",
+                                   "np.concatenate([q2 * c + q1 * s, q1 * c - q2 * s], axis=-1)"),
+}
+
+SWIGLU_MUTANTS = {
+    "swiglu_sigmoid_sign": ("return 1.0 / (1.0 + np.exp(-e))", "return 1.0 / (1.0 + np.exp(e))"),
+    "swiglu_silu_is_sigmoid": ("return e * sigmoid(e)", "return sigmoid(e)"),
+    "swiglu_fwd_f_not_rounded": ("f = _t(silu(e), dtype)", "f = silu(e)"),
+    "swiglu_fwd_h_not_rounded": ("return _t(f * np.asarray(g, dtype=np.float64), dtype)",
+                                 "return f * np.asarray(g, dtype=np.float64)"),
+    "swiglu_bwd_f_not_rounded": ("f = _t(e * s, dtype)", "f = e * s"),
+    "swiglu_bwd_h_not_rounded": ("h = _t(f * g, dtype)", "h = f * g"),
+    "swiglu_df_uses_g": ("df = _t(dh * f, dtype)", "df = _t(dh * g, dtype)"),
+    "swiglu_df_drops_dh": ("df = _t(dh * f, dtype)", "df = _t(f, dtype)"),
+    "swiglu_de_drops_chain": ("de = _t(dh * g * s * (1.0 + e * (1.0 - s)), dtype)", "de = _t(dh * g * s, dtype)"),
+    "swiglu_de_sign": ("de = _t(dh * g * s * (1.0 + e * (1.0 - s)), dtype)",
+                       "de = _t(dh * g * s * (1.0 - e * (1.0 - s)), dtype)"),
+    "swiglu_de_drops_g": ("de = _t(dh * g * s * (1.0 + e * (1.0 - s)), dtype)",
+                          "de = _t(dh * s * (1.0 + e * (1.0 - s)), dtype)"),
+    "swiglu_de_uses_rounded_f": ("de = _t(dh * g * s * (1.0 + e * (1.0 - s)), dtype)",
+                                 "de = _t(dh * g * (s + f * (1.0 - s)), dtype)"),
+    "swiglu_de_not_rounded": ("de = _t(dh * g * s * (1.0 + e * (1.0 - s)), dtype)",
+                              "de = dh * g * s * (1.0 + e * (1.0 - s))"),
+}
+
+
+def _caught(mod, pins):
+    caught = []
+    for pin in pins:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    return caught
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTANTS))
+def test_rope_mutant_is_caught(name):
+    mod = _load_mutant(name, *ROPE_MUTANTS[name], src_path=ROPE_SRC)
+    assert _caught(mod, oracle_pins_rope.ALL_PINS), f"no pin rejects the RoPE mutant {name!r}"
+
+
+@pytest.mark.parametrize("name", sorted(SWIGLU_MUTANTS))
+def test_swiglu_mutant_is_caught(name):
+    src = open(SWIGLU_SRC).read()
+    old, new = SWIGLU_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation {name!r} does not match the oracle source exactly once"
+    # the SwiGLU oracle imports its rounding from the package: load the mutant as a package module
+    mod = types.ModuleType(f"oracle.swiglu_mutant_{name}")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    assert _caught(mod, oracle_pins_swiglu.ALL_PINS), f"no pin rejects the SwiGLU mutant {name!r}"

@@ -72,3 +72,27 @@ def test_layernorm_algorithmic_bytes():
     # fwd = 2MNb + 2Nb + 8M; bwd = 3MNb + Nb + 8M + 8N
     assert wl.ln_algorithmic_bytes(4096, 8192, 2) == {
         "fwd": 134_283_264, "bwd_rows": 201_375_744, "bwd": 201_441_280, "fwd_bwd": 335_724_544}
+
+
+def test_rope_inputs():
+    w = wl.ROPE1.scaled(tokens=300)
+    t = wl.make_rope_inputs(w)
+    assert t["q"].shape == (300, 32, 128) and t["q"].dtype == torch.bfloat16
+    assert t["cos"].shape == (2048, 64) and t["cos"].dtype == torch.float32
+    assert t["positions"].dtype == torch.int32 and t["positions"][257].item() == 257
+    c, s = t["cos"].double(), t["sin"].double()
+    assert torch.allclose(c * c + s * s, torch.ones_like(c), atol=1e-6)  # unit phasors up to fp32 rounding
+    assert torch.all(c[0] == 1) and torch.all(s[0] == 0)
+    r = wl.make_rope_inputs(w.scaled(positions="random", tokens=4096))["positions"]
+    assert r.min() >= 0 and r.max() < 2048 and len(set(r.tolist())) > 1000
+    assert torch.equal(wl.make_rope_inputs(w)["q"].view(torch.int16), t["q"].view(torch.int16))
+
+
+def test_swiglu_inputs():
+    w = wl.SWIGLU1.scaled(M=256, N=1024)
+    t = wl.make_swiglu_inputs(w)
+    assert all(v.shape == (256, 1024) and v.dtype == torch.bfloat16 for v in t.values())
+    e, dh = wl.to_f64(t["e"]), wl.to_f64(t["dh"])
+    assert abs(e.std() - 1) < 0.01 and abs(dh.std() - 0.01) < 2e-4
+    assert wl.swiglu_algorithmic_bytes(11136, 14336, 2) == {"fwd": 957_874_176, "bwd": 1_915_748_352}
+    assert wl.rope_algorithmic_bytes(8192, 32, 128, 2, 2048) == 2 * 8192 * 32 * 128 * 2 + 2 * 2048 * 64 * 4 + 4 * 8192

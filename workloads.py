@@ -169,6 +169,123 @@ def make_inputs(w: Workload) -> dict[str, torch.Tensor]:
     return out
 
 
+# ---------------------------------------------------------------------------
+# RoPE and SwiGLU (the other row/elementwise ops of the Unsloth walkthrough)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class RopeWorkload:
+    """q [tokens, heads, head_dim] rotated in place; cos/sin tables [seq_len, head_dim/2].
+
+    positions: "mod" (token t at position t mod seq_len, i.e. a batch of
+    sequences laid out one after another) or "random" (a seeded draw in
+    [0, seq_len), as for packed sequences of mixed lengths)."""
+
+    name: str
+    dtype: str
+    tokens: int
+    heads: int
+    head_dim: int
+    seq_len: int
+    base: float = 10000.0
+    positions: str = "mod"
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    @property
+    def elsize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def scaled(self, **kw) -> "RopeWorkload":
+        return replace(self, **kw)
+
+
+def make_rope_inputs(w: RopeWorkload) -> dict[str, torch.Tensor]:
+    """q and dq ~ N(0, 1) in ``w.dtype`` [T, H, D]; cos/sin fp32 [seq_len, D/2]
+    from the usual frequency recipe (angle p * base^(-2i/D), computed in
+    float64, stored as fp32); positions int32 [T]."""
+    ss = np.random.SeedSequence(w.seed).spawn(3)
+    rq, rd, rp = (np.random.Generator(np.random.PCG64(s)) for s in ss)
+    shape = (w.tokens, w.heads, w.head_dim)
+    q = rq.standard_normal(size=shape, dtype=np.float32)
+    dq = rd.standard_normal(size=shape, dtype=np.float32)
+    inv = w.base ** (-np.arange(0, w.head_dim, 2, dtype=np.float64) / w.head_dim)
+    ang = np.arange(w.seq_len, dtype=np.float64)[:, None] * inv[None, :]
+    if w.positions == "mod":
+        pos = np.arange(w.tokens, dtype=np.int64) % w.seq_len
+    else:
+        pos = rp.integers(0, w.seq_len, size=w.tokens)
+    out = {"cos": torch.from_numpy(np.cos(ang).astype(np.float32)),
+           "sin": torch.from_numpy(np.sin(ang).astype(np.float32)),
+           "positions": torch.from_numpy(pos.astype(np.int32))}
+    for k, a in (("q", q), ("dq", dq)):
+        t = torch.from_numpy(a)
+        out[k] = t if w.dtype == "f32" else t.to(w.torch_dtype)
+    return out
+
+
+# Llama-7B/8B attention geometry: a batch of 4 sequences of 2048 tokens,
+# 32 query heads of 128 dimensions.
+ROPE1 = RopeWorkload("rope_bf16_8192tok_32x128", "bf16", 4 * 2048, 32, 128, 2048,
+                     note="batch 4 x seq 2048, 32 heads x 128")
+
+
+@dataclass(frozen=True)
+class SwigluWorkload:
+    """e (gate pre-activation), g (up projection) and dh [M, N]."""
+
+    name: str
+    dtype: str
+    M: int
+    N: int
+    e: tuple = ("normal", 0.0, 1.0)
+    g: tuple = ("normal", 0.0, 1.0)
+    dh: tuple = ("normal", 0.0, 1e-2)
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    @property
+    def elsize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def scaled(self, **kw) -> "SwigluWorkload":
+        return replace(self, **kw)
+
+
+def make_swiglu_inputs(w: SwigluWorkload) -> dict[str, torch.Tensor]:
+    ss = np.random.SeedSequence(w.seed).spawn(3)
+    out = {}
+    for k, spec, s in (("e", w.e, ss[0]), ("g", w.g, ss[1]), ("dh", w.dh, ss[2])):
+        a = _draw(np.random.Generator(np.random.PCG64(s)), spec, (w.M, w.N))
+        t = torch.from_numpy(a)
+        out[k] = t if w.dtype == "f32" else t.to(w.torch_dtype)
+    return out
+
+
+# The token count and MLP width of the SwiGLU workload quoted in the packed
+# SwiGLU note ([M, K, N] = [11136, 3584, 14336]): e and g are [11136, 14336].
+SWIGLU1 = SwigluWorkload("swiglu_bf16_11136x14336", "bf16", 11136, 14336, note="M tokens x MLP width 14336")
+
+
+def rope_algorithmic_bytes(tokens: int, heads: int, head_dim: int, elsize: int, seq_len: int) -> int:
+    """One rotation pass: q read and written once, plus the two fp32 tables
+    and (when given) the int32 positions.  Forward and backward are equal."""
+    return 2 * tokens * heads * head_dim * elsize + 2 * seq_len * (head_dim // 2) * 4 + 4 * tokens
+
+
+def swiglu_algorithmic_bytes(M: int, N: int, elsize: int) -> dict[str, int]:
+    """fwd reads e and g and writes h; bwd reads dh, e and g and writes h, df and de."""
+    return {"fwd": 3 * M * N * elsize, "bwd": 6 * M * N * elsize}
+
+
 def algorithmic_bytes(M: int, N: int, elsize: int) -> dict[str, int]:
     """Bytes the method itself must move (no scratch): per pass and in total.
 
