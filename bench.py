@@ -15,7 +15,10 @@ workload on this host.  ``layernorm`` holds the LayerNorm sweep of the
 LayerNorm chapter's benchmark (M = 4096, fp16, N = 1024 .. 15872): per point,
 the forward and the backward (row pass + dw/db reduction) timed per launch
 with events, as GB/s by the chapter's formulas (2 and 3 * numel * elsize per
-launch) and as a fraction of the HBM peak on algorithmic bytes.
+launch) and as a fraction of the HBM peak on algorithmic bytes.  ``rope``
+and ``swiglu`` time the two elementwise ops of the Unsloth walkthrough on
+their workloads (RoPE: 8192 tokens x 32 heads x 128, bf16, in place; SwiGLU:
+11136 x 14336 bf16), forward and backward, per launch with events.
 """
 from __future__ import annotations
 
@@ -53,6 +56,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
     ap.add_argument("--ln-steps", type=int, default=50, help="timed launches per LayerNorm sweep point")
+    ap.add_argument("--no-elementwise", action="store_true", help="skip the RoPE and SwiGLU legs")
     return ap.parse_args()
 
 
@@ -212,6 +216,71 @@ def layernorm_sweep(steps: int) -> dict:
     return {"workload": f"layernorm fp16 M={wl.LN_SWEEP_M}, N = 512*i for i = 2..31", "steps_per_point": steps,
             "median_fwd_frac": round(med("fwd_frac"), 4), "median_bwd_frac": round(med("bwd_frac"), 4),
             "median_bwd_gbps_page_formula": round(med("bwd_gbps_page_formula"), 1), "points": points}
+
+
+def time_launches(fn, steps: int) -> float:
+    """Mean seconds per launch of fn() over `steps` launches bracketed by events."""
+    for _ in range(3):
+        fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e-3 / steps
+
+
+def rope_leg(steps: int) -> dict:
+    import row_normalization_amd as rn
+
+    w = wl.ROPE1
+    t = wl.make_rope_inputs(w)
+    q, cos, sin, pos = t["q"].cuda(), t["cos"].cuda(), t["sin"].cuda(), t["positions"].cuda()
+    L = rn.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), w.tokens, w.heads, w.head_dim, w.heads * w.head_dim, cos.data_ptr(), sin.data_ptr(),
+            w.seq_len, pos.data_ptr(), w.seq_len, DTYPE_CODE[w.dtype], stream)
+
+    def fwd():
+        assert L.rope_fwd(*args) == 0
+
+    def bwd():
+        assert L.rope_bwd(*args) == 0
+
+    t_f, t_b = time_launches(fwd, steps), time_launches(bwd, steps)
+    nbytes = wl.rope_algorithmic_bytes(w.tokens, w.heads, w.head_dim, w.elsize, w.seq_len)
+    return {"workload": w.name, "fwd_us": round(t_f * 1e6, 2), "bwd_us": round(t_b * 1e6, 2),
+            "algorithmic_bytes": nbytes, "fwd_gbps": round(nbytes / t_f / 1e9, 1),
+            "bwd_gbps": round(nbytes / t_b / 1e9, 1), "fwd_frac": round(nbytes / t_f / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_frac": round(nbytes / t_b / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
+def swiglu_leg(steps: int) -> dict:
+    import row_normalization_amd as rn
+
+    w = wl.SWIGLU1
+    t = wl.make_swiglu_inputs(w)
+    e, g, dh = (t[k].cuda() for k in ("e", "g", "dh"))
+    h, df, de = (torch.empty_like(e) for _ in range(3))
+    L = rn.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    code = DTYPE_CODE[w.dtype]
+
+    def fwd():
+        assert L.swiglu_fwd(e.data_ptr(), g.data_ptr(), h.data_ptr(), w.M, w.N, w.N, code, stream) == 0
+
+    def bwd():
+        assert L.swiglu_bwd(dh.data_ptr(), e.data_ptr(), g.data_ptr(), h.data_ptr(), df.data_ptr(), de.data_ptr(),
+                            w.M, w.N, w.N, code, stream) == 0
+
+    t_f, t_b = time_launches(fwd, steps), time_launches(bwd, steps)
+    b = wl.swiglu_algorithmic_bytes(w.M, w.N, w.elsize)
+    return {"workload": w.name, "fwd_us": round(t_f * 1e6, 2), "bwd_us": round(t_b * 1e6, 2),
+            "fwd_gbps": round(b["fwd"] / t_f / 1e9, 1), "bwd_gbps": round(b["bwd"] / t_b / 1e9, 1),
+            "fwd_frac": round(b["fwd"] / t_f / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_frac": round(b["bwd"] / t_b / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": b}
 
 
 def time_steps(path: Path, steps: int) -> float:
@@ -387,6 +456,15 @@ def main():
     del path
     torch.cuda.empty_cache()
     out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_steps)
+    if args.no_elementwise:
+        out["rope"] = out["swiglu"] = None
+    else:
+        out["rope"] = rope_leg(100)
+        print(f"[rope] {out['rope']}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        out["swiglu"] = swiglu_leg(50)
+        print(f"[swiglu] {out['swiglu']}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:

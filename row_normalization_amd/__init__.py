@@ -1,7 +1,8 @@
-"""Fused RMSNorm and LayerNorm forward/backward for the AMD Instinct MI355X (gfx950).
+"""Fused RMSNorm and LayerNorm forward/backward, and the RoPE and SwiGLU
+elementwise ops, for the AMD Instinct MI355X (gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of
-``include/rmsnorm.h`` and ``include/layernorm.h`` (``librmsnorm.so``, built in-tree by
+``include/*.h`` (``librmsnorm.so``, built in-tree by
 ``row_normalization_amd.build``).  This package only marshals arguments to it;
 there is no CPU or PyTorch fallback.
 """
@@ -15,6 +16,10 @@ from ._lib import (
     layernorm_dwdb_reduce,
     layernorm_fwd,
     lib,
+    rope_bwd,
+    rope_fwd,
+    swiglu_bwd,
+    swiglu_fwd,
     rmsnorm_bwd,
     rmsnorm_bwd_rows,
     rmsnorm_bwd_workspace_bytes,
@@ -22,7 +27,8 @@ from ._lib import (
     rmsnorm_fwd,
     rmsnorm_status_string,
 )
-from .autograd import CALLS, LayerNorm, LayerNormFunction, RMSNorm, RMSNormFunction, layernorm, rmsnorm
+from .autograd import (CALLS, LayerNorm, LayerNormFunction, RMSNorm, RMSNormFunction, RoPEFunction, SwiGLUFunction,
+                       layernorm, rmsnorm, rope_embedding, swiglu)
 
 __all__ = [
     "LIB_PATH",
@@ -47,4 +53,12 @@ __all__ = [
     "layernorm",
     "LayerNorm",
     "LayerNormFunction",
+    "rope_fwd",
+    "rope_bwd",
+    "rope_embedding",
+    "RoPEFunction",
+    "swiglu_fwd",
+    "swiglu_bwd",
+    "swiglu",
+    "SwiGLUFunction",
 ]

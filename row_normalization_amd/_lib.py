@@ -1,5 +1,5 @@
-"""ctypes binding of ``librmsnorm.so`` (the C ABI in ``include/rmsnorm.h`` and
-``include/layernorm.h``).
+"""ctypes binding of ``librmsnorm.so`` (the C ABI in ``include/rmsnorm.h``,
+``include/layernorm.h``, ``include/rope.h`` and ``include/swiglu.h``).
 
 Argument marshalling only: tensors are turned into device pointers, shapes,
 row strides, a dtype code and the current HIP stream, and the C status is
@@ -18,7 +18,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librmsnorm.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
-HEADERS = (os.path.join(INCLUDE, "rmsnorm.h"), os.path.join(INCLUDE, "layernorm.h"))
+HEADERS = tuple(os.path.join(INCLUDE, h) for h in ("rmsnorm.h", "layernorm.h", "rope.h", "swiglu.h"))
 
 F32, BF16, F16 = 0, 1, 2
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -51,6 +51,12 @@ _SIGNATURES = {
     "layernorm_dwdb_reduce": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "layernorm_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64,
                                      _c_i64, _c_i64, ctypes.c_int, _c_p]),
+    "rope_fwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_i64, ctypes.c_int,
+                                _c_p]),
+    "rope_bwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_i64, ctypes.c_int,
+                                _c_p]),
+    "swiglu_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p]),
+    "swiglu_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p]),
 }
 
 _lib = None
@@ -61,12 +67,12 @@ class RMSNormError(RuntimeError):
 
 
 def header_functions() -> list[str]:
-    """Names of the functions ``include/rmsnorm.h`` and ``include/layernorm.h`` declare."""
+    """Names of the functions the headers under ``include/`` declare."""
     names = []
     for h in HEADERS:
         with open(h) as f:
             text = f.read()
-        names += re.findall(r"^(?:int|const char\*)\s+((?:rmsnorm|layernorm)_\w+)\s*\(", text, flags=re.M)
+        names += re.findall(r"^(?:int|const char\*)\s+((?:rmsnorm|layernorm|rope|swiglu)_\w+)\s*\(", text, flags=re.M)
     return names
 
 
@@ -291,3 +297,67 @@ def layernorm_bwd(x, weight, dy, mean, rstd, dx, dw, db, workspace, stream=None)
     st = lib().layernorm_bwd(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dw), _ptr(db),
                              _ptr(workspace), wbytes, M, N, stride, _dtype_code(x), _stream(stream))
     _check(st, "layernorm_bwd")
+
+
+# ---------------------------------------------------------------------------
+# RoPE (include/rope.h) and SwiGLU (include/swiglu.h)
+# ---------------------------------------------------------------------------
+
+def _rope_args(q, cos, sin, positions, seq_len):
+    _gpu(q, cos, sin, positions)
+    if q.dim() != 3:
+        raise ValueError("q must be 3-D [tokens, heads, head_dim]")
+    T, H, D = q.shape
+    if D > 1 and q.stride(2) != 1 or H > 1 and q.stride(1) != D:
+        raise ValueError("the heads of a token must be contiguous ([.., heads, head_dim] dense per token)")
+    stride = q.stride(0) if T > 1 else H * D
+    for t, name in ((cos, "cos"), (sin, "sin")):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != D // 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [table_rows, head_dim/2] table")
+    if cos.shape != sin.shape:
+        raise ValueError("cos and sin must have the same shape")
+    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != T or
+                                  not positions.is_contiguous()):
+        raise ValueError("positions must be a contiguous int32 tensor of one entry per token")
+    seq = int(seq_len) if seq_len is not None else cos.shape[0]
+    return T, H, D, stride, cos.shape[0], seq
+
+
+def rope_fwd(q, cos, sin, positions=None, seq_len=None, stream=None) -> None:
+    """Rotates q [tokens, heads, head_dim] in place (pairs are the two head halves)."""
+    T, H, D, stride, rows, seq = _rope_args(q, cos, sin, positions, seq_len)
+    st = lib().rope_fwd(_ptr(q), T, H, D, stride, _ptr(cos), _ptr(sin), rows, _ptr(positions), seq, _dtype_code(q),
+                        _stream(stream))
+    _check(st, "rope_fwd")
+
+
+def rope_bwd(dq, cos, sin, positions=None, seq_len=None, stream=None) -> None:
+    """The inverse rotation (sin negated) of the gradient dq, in place."""
+    T, H, D, stride, rows, seq = _rope_args(dq, cos, sin, positions, seq_len)
+    st = lib().rope_bwd(_ptr(dq), T, H, D, stride, _ptr(cos), _ptr(sin), rows, _ptr(positions), seq,
+                        _dtype_code(dq), _stream(stream))
+    _check(st, "rope_bwd")
+
+
+def _elementwise_layout(ref, others, names):
+    M, N, stride = _rows(ref, names[0])
+    for t, name in zip(others, names[1:]):
+        _same_layout(ref, t, name, stride)
+    return M, N, stride
+
+
+def swiglu_fwd(e, g, h, stream=None) -> None:
+    """h = T(T(silu(e)) * g) over [M, N] (h may be e or g itself)."""
+    _gpu(e, g, h)
+    M, N, stride = _elementwise_layout(e, (g, h), ("e", "g", "h"))
+    st = lib().swiglu_fwd(_ptr(e), _ptr(g), _ptr(h), M, N, stride, _dtype_code(e), _stream(stream))
+    _check(st, "swiglu_fwd")
+
+
+def swiglu_bwd(dh, e, g, h, df, de, stream=None) -> None:
+    """h (recomputed), df = dh * T(f) and de = dh * g * silu'(e); each output may be one of the inputs."""
+    _gpu(dh, e, g, h, df, de)
+    M, N, stride = _elementwise_layout(e, (dh, g, h, df, de), ("e", "dh", "g", "h", "df", "de"))
+    st = lib().swiglu_bwd(_ptr(dh), _ptr(e), _ptr(g), _ptr(h), _ptr(df), _ptr(de), M, N, stride, _dtype_code(e),
+                          _stream(stream))
+    _check(st, "swiglu_bwd")

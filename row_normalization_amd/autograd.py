@@ -10,7 +10,10 @@ was taken), and the Unsloth walkthrough's ``fast_rms_layernorm`` wrapper
 interface of the LayerNorm chapter (chuoer47.github.io), section 2: a
 ``torch.autograd.Function`` called as ``layernorm(x, normalized_shape, weight,
 bias, eps)`` that saves x, weight, bias, mean and rstd and returns
-(dx, None, dw, db, None).
+(dx, None, dw, db, None).  The RoPE adapter follows the walkthrough's
+section 4 (rotate q in place, save only the tables, rotate the gradient back
+with the same kernel); the SwiGLU adapter its section 5 (the forward kernel,
+and one backward kernel giving both input gradients).
 
 Every computation runs in the HIP kernels (``rmsnorm_fwd``, ``rmsnorm_bwd``);
 this module allocates outputs with torch and marshals arguments.  Inputs of
@@ -24,11 +27,12 @@ from __future__ import annotations
 import torch
 
 from ._lib import (layernorm_bwd, layernorm_bwd_workspace_bytes, layernorm_fwd, rmsnorm_bwd,
-                   rmsnorm_bwd_workspace_bytes, rmsnorm_fwd)
+                   rmsnorm_bwd_workspace_bytes, rmsnorm_fwd, rope_bwd, rope_fwd, swiglu_bwd, swiglu_fwd)
 
 # Passes through the adapters (not kernel launches): forward and backward,
 # RMSNorm and LayerNorm counted apart.
-CALLS = {"forward": 0, "backward": 0, "ln_forward": 0, "ln_backward": 0}
+CALLS = {"forward": 0, "backward": 0, "ln_forward": 0, "ln_backward": 0, "rope_forward": 0, "rope_backward": 0,
+         "swiglu_forward": 0, "swiglu_backward": 0}
 
 
 def _rows(t: torch.Tensor) -> torch.Tensor:
@@ -161,3 +165,61 @@ class LayerNorm(torch.nn.Module):
 
     def extra_repr(self) -> str:
         return f"{self.weight.shape[0]}, eps={self.eps}"
+
+
+class RoPEFunction(torch.autograd.Function):
+    """Rotary embedding of q [tokens, heads, head_dim], in place (q is marked
+    dirty and returned); the backward rotates the gradient back."""
+
+    @staticmethod
+    def forward(ctx, q: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, positions=None, seq_len=None):
+        rope_fwd(q, cos, sin, positions, seq_len)
+        ctx.mark_dirty(q)
+        ctx.save_for_backward(cos, sin, positions)
+        ctx.seq_len = seq_len
+        CALLS["rope_forward"] += 1
+        return q
+
+    @staticmethod
+    def backward(ctx, dq: torch.Tensor):
+        cos, sin, positions = ctx.saved_tensors
+        dq = dq.contiguous().clone()  # the incoming gradient may be shared: rotate a private copy in place
+        rope_bwd(dq, cos, sin, positions, ctx.seq_len)
+        CALLS["rope_backward"] += 1
+        return dq, None, None, None, None
+
+
+def rope_embedding(q: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, positions=None, seq_len=None):
+    """In-place rotary embedding of q [tokens, heads, head_dim] (see RoPEFunction)."""
+    return RoPEFunction.apply(q, cos, sin, positions, seq_len)
+
+
+class SwiGLUFunction(torch.autograd.Function):
+    """h = T(T(silu(e)) * g) over [M, N]; the backward gives de and dg from one kernel."""
+
+    @staticmethod
+    def forward(ctx, e: torch.Tensor, g: torch.Tensor):
+        shape = e.shape
+        e2, g2 = e.reshape(-1, shape[-1]).contiguous(), g.reshape(-1, shape[-1]).contiguous()
+        h = torch.empty_like(e2)
+        swiglu_fwd(e2, g2, h)
+        ctx.save_for_backward(e2, g2)
+        ctx.shape = shape
+        CALLS["swiglu_forward"] += 1
+        return h.view(shape)
+
+    @staticmethod
+    def backward(ctx, dh: torch.Tensor):
+        e2, g2 = ctx.saved_tensors
+        dh2 = dh.reshape(e2.shape).contiguous()
+        h = torch.empty_like(e2)
+        dg = torch.empty_like(e2)
+        de = torch.empty_like(e2)
+        swiglu_bwd(dh2, e2, g2, h, dg, de)
+        CALLS["swiglu_backward"] += 1
+        return de.view(ctx.shape), dg.view(ctx.shape)
+
+
+def swiglu(e: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
+    """Elementwise SwiGLU h = silu(e) * g with autograd (see SwiGLUFunction)."""
+    return SwiGLUFunction.apply(e, g)

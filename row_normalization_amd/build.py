@@ -39,8 +39,8 @@ def _run(cmd: list[str]) -> None:
         print(out)
 
 
-HOST_SOURCES = ("rmsnorm_api.cpp", "layernorm_api.cpp")
-KERNEL_SOURCES = ("rmsnorm_kernels.hip", "layernorm_kernels.hip")
+HOST_SOURCES = ("rmsnorm_api.cpp", "layernorm_api.cpp", "elementwise_api.cpp")
+KERNEL_SOURCES = ("rmsnorm_kernels.hip", "layernorm_kernels.hip", "elementwise_kernels.hip")
 
 
 def build(verbose: bool = True) -> str:

@@ -128,9 +128,31 @@ __device__ __forceinline__ void buf_store_f32(const float (&v)[VEC], Rsrc r, uin
   }
 }
 
+// VEC fp32 values from byte offset `off`, in loads of at most 16 bytes.
+template <int VEC, int AUX>
+__device__ __forceinline__ void buf_load_f32(float (&v)[VEC], Rsrc r, uint32_t off) {
+  if constexpr (VEC > 4) {
+#pragma unroll
+    for (int k = 0; k < VEC; k += 4) {
+      // through a 4-float pack, as buf_load does: an implicit conversion of
+      // the builtin's vector result to u32x4_t compiles to a splat of its
+      // first element
+      const Pack<float, 4> q = buf_load<float, 4, AUX>(r, off + k * 4u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[k + j] = q.get(j);
+    }
+  } else {
+    const Pack<float, VEC> p = buf_load<float, VEC, AUX>(r, off);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = p.get(e);
+  }
+}
+
 // Byte offset that is out of range of every descriptor made here (their
-// ranges are below 2^31 bytes).
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+// ranges are below 2^31 bytes).  It sits at 2^31, so a multi-piece access
+// (a 32-byte fp32 vector read as two 16-byte loads) adds its piece offsets
+// to it without wrapping back into range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // Round VEC fp32 values once (to nearest even; gfx950 converts bf16 and fp16
 // pairs in one instruction each) to the storage type S.

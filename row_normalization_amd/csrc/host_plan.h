@@ -51,6 +51,27 @@ struct Span {
 inline Span span(const void* p, int64_t bytes) { return {reinterpret_cast<uintptr_t>(p), static_cast<uintptr_t>(bytes)}; }
 inline bool overlap(Span a, Span b) { return a.len && b.len && a.lo < b.lo + b.len && b.lo < a.lo + a.len; }
 
+// Whether two [M, N] matrices of `es`-byte elements with the same row stride
+// (S elements) at p and q share a byte.  Exact for the row-segment layout:
+// with d = q - p in bytes, row r of p meets row r + k of q iff
+// |d + k * S * es| < N * es, which (N <= S) can only hold for the two k
+// around -d / (S * es).  Lets disjoint interleaved views (the two halves of a
+// fused [M, 2N] buffer) through where a span test would not.
+inline bool matrices_overlap(const void* p, const void* q, int64_t M, int64_t N, int64_t S, int es) {
+  if (M == 0 || N == 0) return false;
+  const int64_t d = static_cast<int64_t>(reinterpret_cast<uintptr_t>(q) - reinterpret_cast<uintptr_t>(p));
+  const int64_t rowb = N * es, sb = S * es;
+  // k1 = ceil(-d / sb): d + k1 * sb lies in [0, sb), d + (k1 - 1) * sb in [-sb, 0)
+  int64_t k1 = -d / sb;
+  if (-d % sb > 0) ++k1;
+  for (int64_t k : {k1, k1 - 1}) {
+    if (k < -(M - 1) || k > M - 1) continue;
+    const int64_t v = d + k * sb;
+    if (v > -rowb && v < rowb) return true;
+  }
+  return false;
+}
+
 inline int64_t matrix_bytes(int64_t M, int64_t N, int64_t stride, int dtype) {
   return M == 0 ? 0 : ((M - 1) * stride + N) * elsize(dtype);
 }

@@ -115,6 +115,44 @@ struct LnBwdArgs {
   int64_t row_iters;
 };
 
+// RoPE: one work item = one token, one group of kRopeGroup heads, one VEC
+// vector of the half-head (and the matching vector of the other half).
+constexpr int kRopeGroup = 4;
+constexpr int kEltThreads = 256;  // workgroup size of the elementwise kernels
+struct RopeArgs {
+  void* q;
+  const float* cos;
+  const float* sin;
+  const int32_t* positions;  // null: t mod seq_len
+  int64_t tokens;
+  int64_t stride;      // elements between tokens
+  int64_t table_rows;
+  int64_t seq_len;
+  int64_t items;       // tokens * groups * nvh
+  int32_t heads;
+  int32_t half;        // head_dim / 2
+  int32_t groups;      // ceil(heads / kRopeGroup)
+  int32_t nvh;         // half / VEC
+  float sin_sign;      // +1 forward, -1 backward
+};
+
+// SwiGLU over [M, N] with one row stride; workgroup b (grid-stride) takes row
+// b / tiles and column tile b mod tiles of kSwigluUnroll * kEltThreads vectors.
+constexpr int kSwigluUnroll = 2;
+struct SwigluArgs {
+  const void* e;
+  const void* g;
+  const void* dh;  // backward only
+  void* h;
+  void* df;        // backward only
+  void* de;        // backward only
+  int64_t M;
+  int64_t stride;
+  int64_t blocks;  // M * tiles
+  int32_t N;
+  int32_t tiles;
+};
+
 // Compiled-in register-array lengths for the row kernels.
 constexpr int kItersSet[] = {1, 2, 4, 5, 8, 16};
 constexpr int kItersMax = 16;
@@ -152,5 +190,8 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
 hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_ln_fwd(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s);
 hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t s);
+hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t s);
+hipError_t launch_swiglu_fwd(int dtype, int vec, const SwigluArgs& a, hipStream_t s);
+hipError_t launch_swiglu_bwd(int dtype, int vec, const SwigluArgs& a, hipStream_t s);
 
 }  // namespace rmsn

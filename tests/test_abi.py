@@ -39,7 +39,8 @@ def test_library_exports_every_declared_symbol(L):
     names = rn.header_functions()
     assert set(names) == {"rmsnorm_fwd", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd_rows", "rmsnorm_dgamma_reduce",
                           "rmsnorm_bwd", "rmsnorm_status_string", "layernorm_fwd", "layernorm_bwd_workspace_bytes",
-                          "layernorm_bwd_rows", "layernorm_dwdb_reduce", "layernorm_bwd"}
+                          "layernorm_bwd_rows", "layernorm_dwdb_reduce", "layernorm_bwd", "rope_fwd", "rope_bwd",
+                          "swiglu_fwd", "swiglu_bwd"}
     for n in names:
         assert hasattr(L, n), n
     dyn = subprocess.run(["nm", "-D", "--defined-only", rn.LIB_PATH], capture_output=True, text=True).stdout
