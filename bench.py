@@ -42,7 +42,10 @@ import workloads as wl  # noqa: E402
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
 METRIC = "RMSNorm fwd+bwd achieved HBM GB/s and % of peak, bf16 M=16384 N=8192"
-KERNEL_SRC = os.path.join(ROOT, "row_normalization_amd", "csrc", "rmsnorm_kernels.hip")
+# the sources the RMSNorm kernels are built from (their fingerprint ties the
+# committed counter summary to the code it was taken on)
+KERNEL_SRCS = tuple(os.path.join(ROOT, "row_normalization_amd", "csrc", f)
+                    for f in ("rmsnorm_kernels.hip", "device_common.h", "launch.h"))
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md")
 
 
@@ -56,13 +59,18 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
     ap.add_argument("--ln-steps", type=int, default=50, help="timed launches per LayerNorm sweep point")
+    ap.add_argument("--ln-ns", type=int, nargs="*", default=None,
+                    help="LayerNorm sweep points (N) to run; default: the chapter's 30 points")
     ap.add_argument("--no-elementwise", action="store_true", help="skip the RoPE and SwiGLU legs")
     return ap.parse_args()
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(h: str):
@@ -186,10 +194,10 @@ class LnPath:
         self.reduce()
 
 
-def layernorm_sweep(steps: int) -> dict:
+def layernorm_sweep(steps: int, ns=None) -> dict:
     """The LayerNorm chapter's sweep: M = 4096 fp16, N = 512 * i, i = 2 .. 31."""
     points = []
-    for N in wl.LN_SWEEP_NS:
+    for N in (ns or wl.LN_SWEEP_NS):
         w = wl.ln_sweep(N)
         path = LnPath(w)
         for _ in range(3):
@@ -455,7 +463,7 @@ def main():
     }
     del path
     torch.cuda.empty_cache()
-    out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_steps)
+    out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_steps, args.ln_ns)
     if args.no_elementwise:
         out["rope"] = out["swiglu"] = None
     else:
