@@ -98,6 +98,15 @@ int check_outputs(std::initializer_list<const void*> ins, std::initializer_list<
 
 SwigluArgs swiglu_args(const void* e, const void* g, const void* dh, void* h, void* df, void* de, int64_t M,
                        int64_t N, int64_t stride, int vec) {
+  int64_t last = N;
+  if (stride == N && M * N > kSwigluFlatRow) {
+    // dense: the same elements as rows of kSwigluFlatRow (a multiple of every
+    // tile length, and of vec, so the last row's length is one as well)
+    const int64_t total = M * N;
+    M = ceil_div(total, kSwigluFlatRow);
+    N = stride = kSwigluFlatRow;
+    last = total - (M - 1) * kSwigluFlatRow;
+  }
   SwigluArgs a{};
   a.e = e;
   a.g = g;
@@ -110,6 +119,7 @@ SwigluArgs swiglu_args(const void* e, const void* g, const void* dh, void* h, vo
   a.N = static_cast<int32_t>(N);
   a.tiles = static_cast<int32_t>(ceil_div(N / vec, int64_t(kSwigluUnroll) * kEltThreads));
   a.blocks = M * a.tiles;
+  a.last_row_elems = last;
   return a;
 }
 

@@ -95,11 +95,11 @@ __device__ __forceinline__ float sigmoid_f32(float e) { return 1.0f / (1.0f + __
 template <typename S, int VEC>
 __global__ __launch_bounds__(kEltThreads) void swiglu_fwd_kernel(const SwigluArgs a) {
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
-  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
   for (int64_t b = blockIdx.x; b < a.blocks; b += gridDim.x) {
     const int64_t row = b / a.tiles;
     const int tile = static_cast<int>(b - row * a.tiles);
     const int64_t off = row * a.stride;
+    const uint32_t row_bytes = static_cast<uint32_t>(row == a.M - 1 ? a.last_row_elems : a.N) * sizeof(S);
     const Rsrc re = make_rsrc(static_cast<const S*>(a.e) + off, row_bytes);
     const Rsrc rg = make_rsrc(static_cast<const S*>(a.g) + off, row_bytes);
     const Rsrc rh = make_rsrc(static_cast<S*>(a.h) + off, row_bytes);
@@ -127,11 +127,11 @@ __global__ __launch_bounds__(kEltThreads) void swiglu_fwd_kernel(const SwigluArg
 template <typename S, int VEC>
 __global__ __launch_bounds__(kEltThreads) void swiglu_bwd_kernel(const SwigluArgs a) {
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
-  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
   for (int64_t b = blockIdx.x; b < a.blocks; b += gridDim.x) {
     const int64_t row = b / a.tiles;
     const int tile = static_cast<int>(b - row * a.tiles);
     const int64_t off = row * a.stride;
+    const uint32_t row_bytes = static_cast<uint32_t>(row == a.M - 1 ? a.last_row_elems : a.N) * sizeof(S);
     const Rsrc rdh = make_rsrc(static_cast<const S*>(a.dh) + off, row_bytes);
     const Rsrc re = make_rsrc(static_cast<const S*>(a.e) + off, row_bytes);
     const Rsrc rg = make_rsrc(static_cast<const S*>(a.g) + off, row_bytes);

@@ -138,7 +138,11 @@ struct RopeArgs {
 
 // SwiGLU over [M, N] with one row stride; workgroup b (grid-stride) takes row
 // b / tiles and column tile b mod tiles of kSwigluUnroll * kEltThreads vectors.
+// Dense operands (row stride == N) are walked as one flat array cut into rows
+// of kSwigluFlatRow elements (a whole number of tiles), so only the very last
+// tile can be partly empty; last_row_elems is the length of the last row.
 constexpr int kSwigluUnroll = 2;
+constexpr int64_t kSwigluFlatRow = 65536;
 struct SwigluArgs {
   const void* e;
   const void* g;
@@ -149,6 +153,7 @@ struct SwigluArgs {
   int64_t M;
   int64_t stride;
   int64_t blocks;  // M * tiles
+  int64_t last_row_elems;
   int32_t N;
   int32_t tiles;
 };
