@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--workload", default="c3", choices=sorted(wl.RMS_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
@@ -405,7 +405,7 @@ def main():
 
         __graft_entry__.build()
     torch.cuda.set_device(0)
-    w = wl.CONFIGS[args.workload]
+    w = wl.RMS_WORKLOADS[args.workload]
     path = Path(w)
     for _ in range(max(args.warmup, 1)):
         path.step()

@@ -22,7 +22,7 @@ def _gpu_available() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) where no GPU is visible; on a GPU machine
+    # GPU tests are skipped (not failed) where no GPU is visible; where one is
     # they run and must load the HIP library, never a fallback.
     if _gpu_available():
         return

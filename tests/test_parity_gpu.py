@@ -35,7 +35,7 @@ def _name_the_case(request):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
 def test_workload_full_size(key):
-    w = wl.CONFIGS[key]
+    w = wl.RMS_WORKLOADS[key]
     run = Run(w)
     diag = compare_with_oracle(run)
     _say(f"{w.name}: partial rows {run.partial_rows}, {diag}")
@@ -128,7 +128,7 @@ def test_inputs_untouched_and_outputs_complete():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("key", ["c2", "c5"])
 def test_bitwise_deterministic(key):
-    w = wl.CONFIGS[key].scaled(M=2048)
+    w = wl.RMS_WORKLOADS[key].scaled(M=2048)
     inputs = wl.make_inputs(w)
     a, b = Run(w, inputs=inputs), Run(w, inputs=inputs)
     for ta, tb in ((a.y, b.y), (a.rstd, b.rstd), (a.dx, b.dx), (a.dgamma, b.dgamma)):

@@ -97,7 +97,7 @@ C4 = Workload("c4_bf16_32768x5120_special_rows", "bf16", 32768, 5120, gamma=("un
 C5 = Workload("c5_bf16_8192x16384", "bf16", 8192, 16384, gamma=("normal", 1.0, 0.1),
               note="wide rows spanning several wavefronts")
 
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+RMS_WORKLOADS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
 HEADLINE = C3
 
 # LayerNorm workloads, with the distributions of the LayerNorm chapter's unit
@@ -116,7 +116,7 @@ def ln_sweep(N: int) -> Workload:
     return Workload(f"ln_f16_{LN_SWEEP_M}x{N}", "f16", LN_SWEEP_M, N, note="GB/s sweep point", **_LN)
 
 
-LN_CONFIGS = {"ln1": LN1, "ln_sweep_8192": ln_sweep(8192)}
+LN_WORKLOADS = {"ln1": LN1, "ln_sweep_8192": ln_sweep(8192)}
 
 
 def _draw(rng: np.random.Generator, spec: tuple, shape) -> np.ndarray:
