@@ -76,8 +76,10 @@ typedef enum {
   RMSNORM_E_ALIGN = -4,     /* a pointer is not aligned to its element size */
   RMSNORM_E_DTYPE = -5,     /* dtype is not RMSNORM_F32 / RMSNORM_BF16 / RMSNORM_F16 */
   RMSNORM_E_EPS = -6,       /* eps is not finite or not > 0 */
-  RMSNORM_E_ALIAS = -7,     /* an output overlaps another buffer (dx == dy is the one allowed case) */
-  RMSNORM_E_WORKSPACE = -8, /* workspace smaller than rmsnorm_bwd_workspace_bytes() */
+  RMSNORM_E_ALIAS = -7,     /* an output overlaps another buffer (for these entry points dx == dy is the
+                               one allowed case; layernorm.h, rope.h and swiglu.h state theirs) */
+  RMSNORM_E_WORKSPACE = -8, /* workspace smaller than rmsnorm_bwd_workspace_bytes() (or
+                               layernorm_bwd_workspace_bytes() for the LayerNorm backward) */
   RMSNORM_E_FLAG = -9,      /* flags has a bit other than RMSNORM_GEMMA | RMSNORM_ROUND_NORMED */
   RMSNORM_E_HIP = -10       /* a HIP launch failed */
 } rmsnorm_status;

@@ -178,13 +178,13 @@ const char* rmsnorm_status_string(int status) {
   switch (status) {
     case RMSNORM_OK: return "ok";
     case RMSNORM_E_NULL: return "a required pointer is NULL";
-    case RMSNORM_E_SHAPE: return "invalid shape (need M >= 0 and 1 <= N <= RMSNORM_N_MAX)";
+    case RMSNORM_E_SHAPE: return "invalid shape (outside the entry point's documented limits, e.g. 1 <= N <= RMSNORM_N_MAX)";
     case RMSNORM_E_STRIDE: return "row stride smaller than N";
     case RMSNORM_E_ALIGN: return "a pointer is not aligned to its element size";
     case RMSNORM_E_DTYPE: return "unsupported dtype (need RMSNORM_F32, RMSNORM_BF16 or RMSNORM_F16)";
     case RMSNORM_E_EPS: return "eps must be finite and > 0";
-    case RMSNORM_E_ALIAS: return "an output overlaps another buffer (only dx == dy is allowed)";
-    case RMSNORM_E_WORKSPACE: return "workspace smaller than rmsnorm_bwd_workspace_bytes()";
+    case RMSNORM_E_ALIAS: return "an output overlaps another buffer (beyond the exact in-place cases the entry point allows)";
+    case RMSNORM_E_WORKSPACE: return "workspace smaller than the matching *_bwd_workspace_bytes() size";
     case RMSNORM_E_FLAG: return "flags may only combine RMSNORM_GEMMA and RMSNORM_ROUND_NORMED";
     case RMSNORM_E_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
