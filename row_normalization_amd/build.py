@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librmsnorm.so")
+EXAMPLE_DIR = os.path.join(ROOT, "tests", "native", "bin")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -70,6 +71,18 @@ def build(verbose: bool = True) -> str:
         print("+", " ".join(link), flush=True)
     _run(link)
     os.replace(tmp, LIB)
+    # a plain C++ caller of the ABI, run by the GPU tests (tests/native/abi_example.cpp)
+    os.makedirs(EXAMPLE_DIR, exist_ok=True)
+    example = [
+        "g++", "-std=c++17", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+        f"-I{os.path.join(ROCM, 'include')}", os.path.join(ROOT, "tests", "native", "abi_example.cpp"),
+        "-o", os.path.join(EXAMPLE_DIR, "abi_example"), f"-L{PKG}", "-lrmsnorm", f"-L{os.path.join(ROCM, 'lib')}",
+        "-lamdhip64", f"-Wl,-rpath,{PKG}", "-Wl,-rpath,$ORIGIN/../../../row_normalization_amd",
+        f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}",
+    ]
+    if verbose:
+        print("+", " ".join(example), flush=True)
+    _run(example)
     return LIB
 
 
