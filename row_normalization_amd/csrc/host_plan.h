@@ -36,6 +36,7 @@ constexpr int64_t kBwdGridMax = 1024;
 // The forward grid is not persistent; it is only capped so that the grid
 // dimension stays small (rows beyond it are taken in further steps).
 constexpr int64_t kFwdGridMax = 1 << 20;
+constexpr int64_t kFwdPersistentMinSteps = 8;
 
 inline int elsize(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
 
@@ -136,7 +137,20 @@ inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int lane_elems, bool bac
   const int64_t groups = ceil_div(M, p.rpb);
   int64_t per_cu = 1;
   while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
-  const int64_t grid_cap = backward ? std::min(kBwdGridMax, kComputeUnits * per_cu) : kFwdGridMax;
+  // The forward is persistent only where that grid fills every CU with
+  // exactly kBwdResidentWaves waves and each workgroup then takes at least
+  // kFwdPersistentMinSteps row groups (its weight stays in registers across
+  // them; measured 2-4 % faster at 16384 x 8192 and 8192 x 16384, 7-9 % for
+  // LayerNorm at 4096 x 8192 and larger).  Elsewhere one workgroup per row
+  // group is faster: 5-wave rows at N = 5120 leave 10 waves per CU (8 %
+  // slower persistent at 32768 x 5120), and with 2-4 row groups per
+  // workgroup (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a
+  // workgroup queue behind each other (3-15 % slower).
+  const bool fwd_persistent = per_cu * p.wpr * p.rpb == kBwdResidentWaves &&
+                              groups >= kFwdPersistentMinSteps * kComputeUnits * per_cu;
+  const int64_t grid_cap = backward         ? std::min(kBwdGridMax, kComputeUnits * per_cu)
+                           : fwd_persistent ? kComputeUnits * per_cu
+                                            : kFwdGridMax;
   p.grid = std::max<int64_t>(1, std::min(groups, grid_cap));
   p.row_iters = ceil_div(groups, p.grid);
   return p;

@@ -48,8 +48,8 @@ constexpr int kLnLoadXdy = kNontemporal;
 constexpr int kLnStoreDx = kNontemporal;
 
 // ---------------------------------------------------------------------------
-// Forward.  Not persistent: the grid covers the row groups (capped, then
-// looped).  weight and bias come from the caches for every row.
+// Forward.  Grid as for the RMSNorm forward (row groups, or persistent where
+// that fills the CUs evenly); weight and bias are loaded once per workgroup.
 // ---------------------------------------------------------------------------
 template <typename S, int VEC, int ITERS>
 __global__ __launch_bounds__(1024) void layernorm_fwd_kernel(const LnFwdArgs a) {
@@ -67,6 +67,15 @@ __global__ __launch_bounds__(1024) void layernorm_fwd_kernel(const LnFwdArgs a) 
   const S* x = static_cast<const S*>(a.x);
   S* y = static_cast<S*>(a.y);
 
+  // weight and bias once per workgroup, kept packed across its rows
+  Pack<S, VEC> wv[ITERS];
+  Pack<S, VEC> bv[ITERS];
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    wv[i] = buf_load<S, VEC, kDefault>(rw, voff + i * iter_bytes);
+    bv[i] = buf_load<S, VEC, kDefault>(rb, voff + i * iter_bytes);
+  }
+
   for (int64_t step = 0; step < a.row_iters; ++step) {
     const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
     const bool active = row < a.M;
@@ -75,14 +84,8 @@ __global__ __launch_bounds__(1024) void layernorm_fwd_kernel(const LnFwdArgs a) 
     const Rsrc ry = make_rsrc(y + off, active ? row_bytes : 0u);
 
     Pack<S, VEC> xv[ITERS];
-    Pack<S, VEC> wv[ITERS];
-    Pack<S, VEC> bv[ITERS];
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) xv[i] = buf_load<S, VEC, kLnLoadX>(rx, voff + i * iter_bytes);
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) wv[i] = buf_load<S, VEC, kDefault>(rw, voff + i * iter_bytes);
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) bv[i] = buf_load<S, VEC, kDefault>(rb, voff + i * iter_bytes);
 
     // pass 1: the mean (vectors past N read as zero and add nothing)
     float s = 0.f;

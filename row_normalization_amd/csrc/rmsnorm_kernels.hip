@@ -64,9 +64,11 @@ constexpr int kBwdStoreDx = kNontemporal;
 
 // ---------------------------------------------------------------------------
 // Forward: y = x * r * w, rstd = r.
-// One step per row group: the grid covers the rows (capped, then looped), so
-// the hardware dispatcher balances the load.  gamma is read per row from the
-// caches (it is N elements, shared by every row).
+// The grid either covers the row groups (one step each; the hardware
+// dispatcher balances the load) or, where that fills the compute units
+// evenly, is persistent (a fixed number of workgroups per CU stepping
+// through the rows).  gamma is loaded once per workgroup and kept packed in
+// registers across its rows.
 // ---------------------------------------------------------------------------
 template <typename S, int VEC, int ITERS>
 __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
@@ -82,6 +84,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
   const S* x = static_cast<const S*>(a.x);
   S* y = static_cast<S*>(a.y);
 
+  // gamma once per workgroup (the same columns for every row it takes)
+  Pack<S, VEC> gv[ITERS];
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) gv[i] = buf_load<S, VEC, kDefault>(rg, voff + i * iter_bytes);
+
   for (int64_t step = 0; step < a.row_iters; ++step) {
     const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
     const bool active = row < a.M;
@@ -89,13 +96,10 @@ __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
     const Rsrc rx = make_rsrc(x + off, active ? row_bytes : 0u);
     const Rsrc ry = make_rsrc(y + off, active ? row_bytes : 0u);
 
-    // all of this lane's loads for the row first: x, then gamma
+    // all of this lane's loads for the row before any arithmetic
     Pack<S, VEC> xv[ITERS];
-    Pack<S, VEC> gv[ITERS];
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) xv[i] = buf_load<S, VEC, kFwdLoadX>(rx, voff + i * iter_bytes);
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) gv[i] = buf_load<S, VEC, kDefault>(rg, voff + i * iter_bytes);
 
     float ss = 0.f;
 #pragma unroll
