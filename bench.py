@@ -43,7 +43,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
 METRIC = "RMSNorm fwd+bwd achieved HBM GB/s and % of peak, bf16 M=16384 N=8192"
 # the sources the RMSNorm kernels are built from (their fingerprint ties the
-# committed counter summary to the code it was taken on)
+# committed counter summary to the code it was taken on; comments excluded)
 KERNEL_SRCS = tuple(os.path.join(ROOT, "row_normalization_amd", "csrc", f)
                     for f in ("rmsnorm_kernels.hip", "device_common.h", "launch.h"))
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md")
@@ -66,10 +66,16 @@ def parse():
 
 
 def kernel_hash() -> str:
+    """Fingerprint of the code the RMSNorm kernels are built from: the
+    sources with comments and blank lines removed, so that an edit of a
+    comment does not invalidate counters taken on the same code."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 
 

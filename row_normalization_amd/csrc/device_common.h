@@ -1,7 +1,7 @@
-// Device-side building blocks shared by the row kernels (RMSNorm and
-// LayerNorm): packed row vectors, raw-buffer access with hardware range
-// checks, rounding to the I/O types, and the wave / row-group reductions.
-// Included by the .hip files only.
+// Device-side building blocks shared by every kernel of the library (RMSNorm,
+// LayerNorm, RoPE, SwiGLU): packed vectors, raw-buffer access with hardware
+// range checks, rounding to the I/O types, the wave / row-group reductions
+// and the dispatch helper.  Included by the .hip files only.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -10,7 +10,7 @@
 // How it maps to the hardware.  The work is a bandwidth-bound row reduction
 // (about 1 flop per byte), so there is no MFMA: everything is about moving
 // each byte of x, dy, y and dx through HBM exactly once.
-//  - Each lane owns whole 16-byte column vectors of a row (8 bf16 or 4 fp32)
+//  - Each lane owns whole 16-byte column vectors of a row (8 bf16/fp16 or 4 fp32)
 //    and issues all of its loads for the row before any arithmetic; a row is
 //    read once and never re-read.
 //  - Every row access is a raw buffer load/store through a per-row buffer
@@ -22,7 +22,7 @@
 //    branch-guarded loads it has to wait for all of them, which serialises
 //    the backward's row pipeline).
 //  - Upcast to fp32 on load; sums in fp32; one rounding (RNE, the gfx950
-//    packed bf16 convert) on store.
+//    packed bf16/fp16 converts) on store.
 //  - Row sums are reduced inside the wave with DPP row operations, a
 //    ds_swizzle across the 32-lane halves and two readlanes (no LDS traffic).
 //    When a row spans several waves the per-wave sums meet in LDS behind one
@@ -30,8 +30,8 @@
 //    per row suffices.
 //  - The backward is a persistent grid: each workgroup owns a fixed set of
 //    rows, keeps the weight and its dgamma column partials in registers
-//    across them, and writes one fp32 partial row at the end (row groups of the workgroup
-//    are combined in LDS in a fixed order).  A second small kernel sums the
+//    across them, and writes one fp32 partial row at the end (row groups of
+//    the workgroup are combined in LDS in a fixed order).  A second small kernel sums the
 //    partial rows per column in a fixed order.  No atomics touch data, so
 //    every result is bitwise reproducible.
 //  - dx may be written over dy: each lane reads its own dy elements before it
