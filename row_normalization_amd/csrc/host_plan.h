@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <initializer_list>
 #include <limits>
+#include <tuple>
 
 #include "launch.h"
 #include "rmsnorm.h"
@@ -97,29 +98,45 @@ inline int choose_vec(int dtype, int64_t N, int64_t stride, std::initializer_lis
   return 1;
 }
 
-// Waves per row and vectors per lane: among 1..16 waves per row and the
-// compiled register-array lengths, the shape that wastes the fewest lanes;
-// ties go to the length nearest `target` vectors per lane, then to fewer waves.
-inline bool row_shape(int64_t nvec, int iters_cap, int target, int* wpr, int* iters) {
-  int64_t best_waste = -1;
-  int best_dist = 0;
+// Waves per row and vectors per lane.  Candidates: 1..16 waves per row, a
+// compiled register-array length within the lane's register budget, no wave
+// without work.  The smallest key wins, compared in this order:
+//   1. waste (covered minus real vectors) above a quarter of the row;
+//   2. one vector per lane in a row of more than two waves;
+//   3. 16-bit I/O, forward: a row of more than kFwdRowWaves waves;
+//   4. 16-bit I/O: distance from `target` vectors per lane, then waste;
+//      fp32 I/O: waste, then distance from `target`;
+//   5. fewer waves.
+// Measured on MI355X (forward and backward, M = 4096 and 16384): one vector
+// per lane in rows of 9-15 waves ran 15-40 % slower than two vectors in
+// half as many waves with a partly empty last wave (e.g. bf16 16384 x 7680
+// forward 129 -> 82 us); 16-bit rows of 10-16 waves in the forward 7-17 %
+// slower than 5-8 waves with 4 vectors; for fp32 rows, where a vector holds
+// half the elements, the least waste was within 2 % of the best shape and the
+// 16-bit order up to 6 % slower.
+inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool backward, int* wpr, int* iters) {
+  bool found = false;
+  std::tuple<bool, bool, bool, int64_t, int64_t, int> best{};
   for (int w = 1; w <= kMaxBlockWaves; ++w) {
     for (int it : kItersSet) {
       if (it > iters_cap || int64_t(it) * kWave * w < nvec) continue;
+      if (w > 1 && int64_t(it) * kWave * (w - 1) >= nvec) continue;
       const int64_t waste = int64_t(it) * kWave * w - nvec;
-      const int dist = it > target ? it - target : target - it;
-      if (best_waste < 0 || waste < best_waste || (waste == best_waste && dist < best_dist)) {
-        best_waste = waste;
-        best_dist = dist;
+      const int64_t dist = it > target ? it - target : target - it;
+      const auto key = std::make_tuple(waste * 4 > nvec, it == 1 && w > 2, narrow && !backward && w > kFwdRowWaves,
+                                       narrow ? dist : waste, narrow ? waste : dist, w);
+      if (!found || key < best) {
+        found = true;
+        best = key;
         *wpr = w;
         *iters = it;
       }
     }
   }
-  return best_waste >= 0;
+  return found;
 }
 
-inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int lane_elems, bool backward) {
+inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int es, int lane_elems, bool backward) {
   RowPlan p{};
   p.vec = vec;
   const int64_t nvec = N / vec;
@@ -129,7 +146,7 @@ inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int lane_elems, bool bac
   // 4 % faster than 16 x 2); the backward keeps kLaneVectors.
   const int target =
       backward ? kLaneVectors : static_cast<int>(std::max<int64_t>(kLaneVectors, ceil_div(nvec, int64_t(kWave) * kFwdRowWaves)));
-  if (!row_shape(nvec, cap, target, &p.wpr, &p.iters)) {
+  if (!row_shape(nvec, cap, target, es == 2, backward, &p.wpr, &p.iters)) {
     p.iters = 0;  // cannot happen for N <= RMSNORM_N_MAX
     return p;
   }

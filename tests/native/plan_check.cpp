@@ -20,7 +20,7 @@ int main() {
           if (N % vec) continue;
           const bool bwd = op == RowOp::kRmsBwd || op == RowOp::kLnBwd;
           for (int64_t M : {int64_t(1), int64_t(4096), int64_t(1) << 20}) {
-            const RowPlan p = plan_rows(M, N, vec, lane_elems_cap(op, elsize(dt)), bwd);
+            const RowPlan p = plan_rows(M, N, vec, elsize(dt), lane_elems_cap(op, elsize(dt)), bwd);
             ++n;
             const int64_t lds = p.rpb > 1 ? (op == RowOp::kLnBwd ? 8 : 4) * N : 0;
             const bool ok = p.iters > 0 && p.vec * p.iters <= lane_elems_cap(op, elsize(dt)) && p.threads() <= 1024 &&
