@@ -256,12 +256,31 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
       for (int i = 0; i < ITERS; ++i) {
         const int v = (i * a.wpr + L.wv) * kWave + L.lane;
         if (v < a.nvec) {
+          float* cw = comb + v * VEC;
+          float* cb = comb + a.N + v * VEC;
+          if (g == 0) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            float* cw = comb + v * VEC + e;
-            float* cb = cw + a.N;
-            *cw = (g == 0) ? accw[i][e] : *cw + accw[i][e];
-            *cb = (g == 0) ? accb[i][e] : *cb + accb[i][e];
+            for (int e = 0; e < VEC; ++e) {
+              cw[e] = accw[i][e];
+              cb[e] = accb[i][e];
+            }
+          } else {
+            // Both tables' cells are read before either is written: the
+            // compiler cannot tell that the dw and db rows do not overlap,
+            // so interleaved read-add-write steps would each wait out the
+            // LDS latency (measured: 4096 x 1024 fp16, 8 row groups per
+            // workgroup, 15.9 -> 10.5 us).
+            float tw[VEC], tb[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              tw[e] = cw[e];
+              tb[e] = cb[e];
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              cw[e] = tw[e] + accw[i][e];
+              cb[e] = tb[e] + accb[i][e];
+            }
           }
         }
       }
