@@ -11,7 +11,8 @@ Prints ONE JSON line.  ``value`` is algorithmic bytes of fwd+bwd per step
 divided by the measured step time; ``roofline`` describes the dominant kernel
 (the backward row pass) timed per launch with HIP events on the same stream;
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
-workload on this host.  ``layernorm`` holds the LayerNorm sweep of the
+workload on this host, on one core (``value``) and sharded over up to 16
+cores (``all_cores``).  ``layernorm`` holds the LayerNorm sweep of the
 LayerNorm chapter's benchmark (M = 4096, fp16, N = 1024 .. 15872): per point,
 the forward and the backward (row pass + dw/db reduction) timed per launch
 with events, as GB/s by the chapter's formulas (2 and 3 * numel * elsize per
@@ -42,10 +43,11 @@ import workloads as wl  # noqa: E402
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
 METRIC = "RMSNorm fwd+bwd achieved HBM GB/s and % of peak, bf16 M=16384 N=8192"
-# the sources the RMSNorm kernels are built from (their fingerprint ties the
-# committed counter summary to the code it was taken on; comments excluded)
+# the sources the RMSNorm kernels and their launch plans are built from (their
+# fingerprint ties the committed counter summary to the code it was taken on;
+# comments excluded)
 KERNEL_SRCS = tuple(os.path.join(ROOT, "row_normalization_amd", "csrc", f)
-                    for f in ("rmsnorm_kernels.hip", "device_common.h", "launch.h"))
+                    for f in ("rmsnorm_kernels.hip", "device_common.h", "launch.h", "host_plan.h"))
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md")
 
 
@@ -57,6 +59,8 @@ def parse():
     ap.add_argument("--workload", default="c3", choices=sorted(wl.RMS_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-all-cores-seconds", type=float, default=8.0,
+                    help="wall time of the oracle sample sharded over the host's cores (0: skip)")
     ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
     ap.add_argument("--ln-steps", type=int, default=50, help="timed launches per LayerNorm sweep point")
     ap.add_argument("--ln-ns", type=int, nargs="*", default=None,
@@ -309,24 +313,18 @@ def time_steps(path: Path, steps: int) -> float:
     return s.elapsed_time(e) * 1e-3 / steps
 
 
-def time_kernels(path: Path, steps: int) -> dict:
-    """Average duration of each launch, from events recorded between the launches."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for k in range(steps):
-        ev[k][0].record()
-        path.fwd()
-        ev[k][1].record()
-        path.bwd_rows()
-        ev[k][2].record()
-        path.reduce()
-        ev[k][3].record()
-    torch.cuda.synchronize()
-    names = ["fwd", "bwd_rows", "dgamma_reduce"]
+def time_kernels(path, steps: int) -> dict:
+    """Average duration of each launch of the step: `steps` back-to-back
+    launches of that kernel alone, bracketed by one pair of events.
+
+    Events recorded between every two launches would each add a marker packet
+    and about 2-6 us of dispatch gap to the launch after it; back to back, the
+    figure agrees with rocprofv3's kernel durations.  Repeating a launch reads
+    and writes the same buffers as the step does (in place, the backward
+    consumes the previous launch's dx as its dy)."""
     out = {}
-    for i, n in enumerate(names):
-        d = [ev[k][i].elapsed_time(ev[k][i + 1]) * 1e-3 for k in range(steps)]
-        out[n] = {"mean_s": float(np.mean(d)), "median_s": float(np.median(d))}
+    for name, fn in (("fwd", path.fwd), ("bwd_rows", path.bwd_rows), ("dgamma_reduce", path.reduce)):
+        out[name] = {"mean_s": time_launches(fn, steps)}
     return out
 
 
@@ -371,28 +369,69 @@ def copy_reference(nbytes: int, steps: int) -> float:
     return 2 * nbytes / t / 1e9
 
 
-def cpu_baseline(w: wl.Workload, seconds: float) -> dict:
-    """The fp64 oracle (as it stands) on a sample of rows of the same workload."""
+_ORACLE_SAMPLE = None
+
+
+def _oracle_sample_init(w: wl.Workload, rows: int):
+    """Pool initializer: the worker's own copy of the sample, upcast to fp64."""
+    global _ORACLE_SAMPLE
+    t = wl.make_inputs(w.scaled(M=rows))
+    _ORACLE_SAMPLE = (w, *(wl.to_f64(t[k]) for k in ("x", "gamma", "dy")))
+
+
+def _oracle_sample_pass(_=None) -> int:
+    """One fwd + bwd of the oracle over the sample."""
     import oracle
 
+    w, x, g, dy = _ORACLE_SAMPLE
+    oracle.forward(x, g, w.eps, w.gemma)
+    oracle.backward(x, g, dy, w.eps, w.gemma)
+    return 1
+
+
+def oracle_all_cores(w: wl.Workload, rows: int, seconds: float) -> dict:
+    """The same oracle sample, row-sharded over the host's cores.
+
+    One process per core (at most 16), each holding its own copy of the
+    sample; the timed region covers whole batches of one pass per worker
+    after every worker has done one untimed pass.  Workers are spawned (not
+    forked), so they share no state with this process's HIP runtime.
+    """
+    import multiprocessing as mp
+
+    k = max(1, min(len(os.sched_getaffinity(0)), 16))
+    with mp.get_context("spawn").Pool(k, initializer=_oracle_sample_init, initargs=(w, rows)) as pool:
+        pool.map(_oracle_sample_pass, range(k), chunksize=1)
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            passes += sum(pool.map(_oracle_sample_pass, range(k), chunksize=1))
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    nbytes = wl.algorithmic_bytes(rows, w.N, w.elsize)["fwd_bwd"] * passes
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": k, "kind": "oracle",
+            "sample": f"{passes} passes of fwd+bwd over {rows} rows x N={w.N}, {k} worker processes, "
+                      f"{el:.1f} s"}
+
+
+def cpu_baseline(w: wl.Workload, seconds: float, all_cores_seconds: float) -> dict:
+    """The fp64 oracle (as it stands) on a sample of rows of the same workload."""
     rows = min(w.M, 1024)
-    sample = w.scaled(M=rows)
-    t = wl.make_inputs(sample)
-    x, g, dy = (wl.to_f64(t[k]) for k in ("x", "gamma", "dy"))
+    _oracle_sample_init(w, rows)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(x, g, w.eps, w.gemma)
-        oracle.backward(x, g, dy, w.eps, w.gemma)
-        reps += 1
+        reps += _oracle_sample_pass()
         el = time.perf_counter() - t0
         if el >= seconds and reps >= 2:
             break
     per = el / reps
     nbytes = wl.algorithmic_bytes(rows, w.N, w.elsize)["fwd_bwd"]
-    return {"value": nbytes / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {w.M} rows x N={w.N} ({w.dtype} inputs upcast to fp64), fwd+bwd repeated {reps}x "
-                      f"in {el:.1f} s; numpy elementwise ops, single thread; {per * 1e3:.1f} ms per sample",
-            "host_cpus_visible": len(os.sched_getaffinity(0))}
+    out = {"value": nbytes / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{rows} of {w.M} rows x N={w.N} ({w.dtype} inputs upcast to fp64), fwd+bwd repeated {reps}x "
+                     f"in {el:.1f} s; numpy elementwise ops, single thread; {per * 1e3:.1f} ms per sample",
+           "host_cpus_visible": len(os.sched_getaffinity(0))}
+    out["all_cores"] = oracle_all_cores(w, rows, all_cores_seconds) if all_cores_seconds > 0 else None
+    return out
 
 
 def main():
@@ -480,7 +519,7 @@ def main():
         print(f"[swiglu] {out['swiglu']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.cpu_all_cores_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
