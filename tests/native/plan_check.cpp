@@ -2,8 +2,10 @@
 // every row operation, dtype, vector width and N in [1, RMSNORM_N_MAX], at
 // three row counts: a plan always exists, covers every column and row, keeps
 // a lane's row data within the register model, fits a 1024-thread workgroup,
-// and keeps the LDS combine buffer within 64 KB.  Built and run by
-// tests/test_plan.py; prints one summary line and exits non-zero on failure.
+// and keeps the LDS combine buffer within 64 KB.  It also pins the row shapes
+// the planner picks for a few widths where the ordering of its rules
+// matters.  Built and run by tests/test_plan.py; prints one summary line and
+// exits non-zero on failure.
 #include <cstdio>
 
 #include "host_plan.h"
@@ -32,6 +34,33 @@ int main() {
                           static_cast<long>(p.grid));
           }
         }
+  // (element size, N, op, waves per row, vectors per lane), 16-byte vectors
+  struct Pin {
+    int es;
+    int64_t N;
+    RowOp op;
+    int wpr, iters;
+  };
+  const Pin pins[] = {
+      {2, 8192, RowOp::kRmsFwd, 8, 2},   {2, 8192, RowOp::kRmsBwd, 8, 2},    // no waste
+      {2, 7680, RowOp::kRmsFwd, 8, 2},   {2, 7680, RowOp::kLnBwd, 8, 2},     // not 15 x 1
+      {2, 2560, RowOp::kLnFwd, 3, 2},    {2, 4608, RowOp::kRmsBwd, 5, 2},    // not 5 x 1, 9 x 1
+      {2, 16384, RowOp::kRmsFwd, 8, 4},  {2, 16384, RowOp::kRmsBwd, 16, 2},  // forward rows of <= 8 waves
+      {2, 13312, RowOp::kLnFwd, 7, 4},   {2, 13312, RowOp::kLnBwd, 13, 2},
+      {2, 1536, RowOp::kRmsFwd, 3, 1},                                        // 2 x 2 would waste a quarter
+      {4, 14848, RowOp::kRmsFwd, 12, 5}, {4, 7680, RowOp::kRmsFwd, 6, 5},    // fp32: least waste first
+      {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
+  };
+  for (const Pin& q : pins) {
+    const bool bwd = q.op == RowOp::kRmsBwd || q.op == RowOp::kLnBwd;
+    const RowPlan p = plan_rows(4096, q.N, 16 / q.es, q.es, lane_elems_cap(q.op, q.es), bwd);
+    ++n;
+    if (p.wpr != q.wpr || p.iters != q.iters) {
+      ++bad;
+      std::printf("shape pin: es=%d N=%ld op=%d: got %d x %d, expected %d x %d\n", q.es, static_cast<long>(q.N),
+                  static_cast<int>(q.op), p.wpr, p.iters, q.wpr, q.iters);
+    }
+  }
   std::printf("checked %ld plans, %ld bad\n", n, bad);
   return bad ? 1 : 0;
 }

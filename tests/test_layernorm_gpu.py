@@ -40,6 +40,8 @@ SMALL = [
     ("f32", 1, 1), ("f32", 3, 7), ("f32", 17, 33), ("f32", 64, 128), ("f32", 130, 1000), ("f32", 9, 16384),
     ("bf16", 1, 1), ("bf16", 5, 2), ("bf16", 33, 5120), ("bf16", 257, 4096), ("bf16", 20, 12288),
     ("f16", 2, 3), ("f16", 31, 96), ("f16", 100, 1024), ("f16", 1030, 1536), ("f16", 7, 15872), ("f16", 5, 16384),
+    # partly empty last waves (planner's choice)
+    ("f16", 67, 7680), ("bf16", 45, 2560), ("f16", 300, 3584), ("f16", 29, 13312), ("f32", 23, 3328),
 ]
 
 

@@ -88,6 +88,12 @@ SMALL = [
     ("f16", 100, 16384, False, False),
     ("f16", 4096, 4096, False, False),
     ("f16", 7, 12, False, True),
+    # shapes whose last wave is partly empty by the planner's choice
+    ("bf16", 67, 7680, True, True),     # 8 waves x 2 vectors, 64 of 1024 vectors empty
+    ("f16", 45, 2560, False, False),    # 3 x 2, two row groups per workgroup
+    ("bf16", 300, 3584, True, False),   # 4 x 2
+    ("bf16", 129, 13312, False, False), # forward 7 x 4 (128 empty), backward 13 x 2
+    ("f32", 23, 3328, False, False),    # fp32 7 x 2 rather than 13 x 1
 ]
 
 
