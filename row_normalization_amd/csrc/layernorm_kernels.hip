@@ -43,9 +43,9 @@ using namespace dev;
 
 // Streamed operands are touched once per pass: nontemporal, as for RMSNorm.
 constexpr int kLnLoadX = kNontemporal;
-constexpr int kLnStoreY = kNontemporal;
+constexpr int kLnStoreY = kStreamStore;
 constexpr int kLnLoadXdy = kNontemporal;
-constexpr int kLnStoreDx = kNontemporal;
+constexpr int kLnStoreDx = kStreamStore;
 
 // ---------------------------------------------------------------------------
 // Forward.  Grid as for the RMSNorm forward (row groups, or persistent where
