@@ -175,6 +175,16 @@ inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int es, int lane_elems, 
 
 inline int64_t partial_rows_bound(int64_t M) { return std::min(M, kBwdGridMax); }
 
+// Whether a backward workgroup should keep the next row's loads in flight
+// while it works on a row: only where one workgroup fills its CU's resident
+// waves, so no other workgroup's loads cover the row's reduction and barrier.
+// Measured on MI355X (bf16): 8192 x 16384, 8192 x 15872, 16384 x 15360 and
+// 16384 x 9216 row passes 5-9 % faster pipelined; with two workgroups per CU
+// (16384 x 8192, 32768 x 5120) pipelining was 2-8 % slower.
+inline bool bwd_pipelined(const RowPlan& p, int es) {
+  return p.wpr * p.rpb * 2 > kBwdResidentWaves && bwd_pipeline_fits(p.vec, p.iters, es);
+}
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_E_HIP; }
 
 }  // namespace rmsn

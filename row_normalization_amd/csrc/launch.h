@@ -63,6 +63,7 @@ struct BwdArgs {
   int32_t wpr;
   int32_t rpb;
   int64_t row_iters;
+  int32_t pipeline;  // 1: keep the next row's loads in flight during a row's work
 };
 
 // Column sums of one or two [rows, N] fp32 tables stored back to back
@@ -113,6 +114,7 @@ struct LnBwdArgs {
   int32_t wpr;
   int32_t rpb;
   int64_t row_iters;
+  int32_t pipeline;  // as in BwdArgs
 };
 
 // RoPE: one work item = one token, one group of kRopeGroup heads, one VEC
@@ -181,6 +183,15 @@ constexpr int lane_elems_cap(RowOp op, int elsize) {
                               : op == RowOp::kRmsBwd ? 2 * elsize + 8
                               : op == RowOp::kLnFwd  ? 3 * elsize + 1
                                                      : 2 * elsize + 12);
+}
+
+// The backwards' pipelined row loop keeps a second row's x and dy in
+// registers.  It is compiled, and chosen, only where a lane holds at most
+// two 16-byte vectors of each operand (a vector narrower than a register
+// still takes a whole one): beyond that the second row would spill.
+constexpr int kPipelineLaneBytes = 32;
+constexpr bool bwd_pipeline_fits(int vec, int iters, int elsize) {
+  return iters * (vec * elsize > 4 ? vec * elsize : 4) <= kPipelineLaneBytes;
 }
 
 // Tile of the dgamma reduction: kReduceCols column threads (a 128-byte row

@@ -75,6 +75,7 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
+  a.pipeline = bwd_pipelined(p, elsize(dtype));
   const int st = hip_status(launch_ln_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;
   return st;

@@ -147,26 +147,115 @@ __global__ __launch_bounds__(1024) void layernorm_fwd_kernel(const LnFwdArgs a) 
 // keeps, for the columns it owns, w in fp32 and its dw and db partials in
 // fp32 registers across all of its rows.
 // ---------------------------------------------------------------------------
+// One row's operands as a lane holds them between its loads and its work.
+template <typename S, int VEC, int ITERS>
+struct LnBwdRow {
+  Pack<S, VEC> x[ITERS];
+  Pack<S, VEC> dy[ITERS];
+  float mean;
+  float rstd;
+};
+
+// Offsets and descriptors a backward lane uses for every row.
+struct LnBwdGeom {
+  uint32_t voff;        // byte offset of the lane's first vector in a row
+  uint32_t iter_bytes;  // bytes between the lane's successive vectors
+  uint32_t row_bytes;   // N * sizeof(S)
+  Rsrc mean;            // the M saved means
+  Rsrc rstd;            // the M saved rstd values
+};
+
+template <typename S, int VEC, int ITERS>
+__device__ __forceinline__ void ln_bwd_load_row(LnBwdRow<S, VEC, ITERS>& t, const LnBwdArgs& a, int64_t step,
+                                                const Lane& L, const LnBwdGeom& G) {
+  const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
+  const bool active = row < a.M;
+  const int64_t off = active ? row * a.stride : 0;
+  const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? G.row_bytes : 0u);
+  const Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + off, active ? G.row_bytes : 0u);
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    t.x[i] = buf_load<S, VEC, kLnLoadXdy>(rx, G.voff + i * G.iter_bytes);
+    t.dy[i] = buf_load<S, VEC, kLnLoadXdy>(rd, G.voff + i * G.iter_bytes);
+  }
+  // mean and rstd of a missing row read as zero (out of the descriptors' range)
+  const uint32_t soff = active ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+  t.mean = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(G.mean, soff, 0, kDefault));
+  t.rstd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(G.rstd, soff, 0, kDefault));
+}
+
+template <typename S, int VEC, int ITERS>
+__device__ __forceinline__ void ln_bwd_process_row(LnBwdRow<S, VEC, ITERS>& t, const LnBwdArgs& a, int64_t step,
+                                                   const float (&w)[ITERS][VEC], float (&accw)[ITERS][VEC],
+                                                   float (&accb)[ITERS][VEC], float (*red)[2][kMaxBlockWaves],
+                                                   const Lane& L, const LnBwdGeom& G) {
+  const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
+  const bool active = row < a.M;
+  const int64_t off = active ? row * a.stride : 0;
+  // dx may be the dy buffer itself; every element of dy this lane owns was
+  // loaded into registers before this point
+  const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + off, active ? G.row_bytes : 0u);
+  const float mean = t.mean, rstd = t.rstd;
+
+  // the two row sums: of x_hat * g and of g, with g = w * dy
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float xh = (t.x[i].get(e) - mean) * rstd;
+      const float g = w[i][e] * t.dy[i].get(e);
+      s1 = fmaf(xh, g, s1);
+      s2 += g;
+    }
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    t.x[i].keep_packed();
+    t.dy[i].keep_packed();
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (a.wpr > 1) group_sum2(s1, s2, red, step, L.wave, L.group, a.wpr, L.lane);
+  const float c1 = s1 * a.inv_n;
+  const float c2 = s2 * a.inv_n;
+
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float df = t.dy[i].get(e);
+      const float xh = (t.x[i].get(e) - mean) * rstd;
+      o[e] = (w[i][e] * df - fmaf(xh, c1, c2)) * rstd;
+      accw[i][e] = fmaf(df, xh, accw[i][e]);
+      accb[i][e] += df;
+    }
+    buf_store<S, VEC, kLnStoreDx>(round_pack<S, VEC>(o), rdx, G.voff + i * G.iter_bytes);
+  }
+}
+
 template <typename S, int VEC, int ITERS>
 __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float comb[];  // 2N floats, when rpb > 1
   __shared__ float red[2][2][kMaxBlockWaves];
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
   const Lane L(a.wpr);
-  const uint32_t voff = L.first_vec() * kPack;
-  const uint32_t iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
-  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
-  const Rsrc rmean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
-  const Rsrc rrstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+  LnBwdGeom G;
+  G.voff = L.first_vec() * kPack;
+  G.iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
+  G.row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  G.mean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
+  G.rstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+  const uint32_t voff = G.voff;
 
   float w[ITERS][VEC];
   float accw[ITERS][VEC];
   float accb[ITERS][VEC];
   {
-    const Rsrc rw = make_rsrc(a.weight, row_bytes);
+    const Rsrc rw = make_rsrc(a.weight, G.row_bytes);
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-      const Pack<S, VEC> g = buf_load<S, VEC, kDefault>(rw, voff + i * iter_bytes);
+      const Pack<S, VEC> g = buf_load<S, VEC, kDefault>(rw, voff + i * G.iter_bytes);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         w[i][e] = g.get(e);
@@ -176,60 +265,82 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
     }
   }
 
-  for (int64_t step = 0; step < a.row_iters; ++step) {
-    const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
-    const bool active = row < a.M;
-    const int64_t off = active ? row * a.stride : 0;
-    const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? row_bytes : 0u);
-    const Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + off, active ? row_bytes : 0u);
-    const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + off, active ? row_bytes : 0u);
-
-    Pack<S, VEC> xv[ITERS];
-    Pack<S, VEC> dv[ITERS];
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      xv[i] = buf_load<S, VEC, kLnLoadXdy>(rx, voff + i * iter_bytes);
-      dv[i] = buf_load<S, VEC, kLnLoadXdy>(rd, voff + i * iter_bytes);
-    }
-    // mean and rstd of a missing row read as zero (out of the descriptors' range)
-    const uint32_t soff = active ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
-    const float mean = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rmean, soff, 0, kDefault));
-    const float rstd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrstd, soff, 0, kDefault));
-
-    // the two row sums: of x_hat * g and of g, with g = w * dy
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float xh = (xv[i].get(e) - mean) * rstd;
-        const float g = w[i][e] * dv[i].get(e);
-        s1 = fmaf(xh, g, s1);
-        s2 += g;
+  bool pipelined = false;
+  if constexpr (bwd_pipeline_fits(VEC, ITERS, sizeof(S))) pipelined = a.pipeline;
+  if (pipelined) {
+    // One workgroup per CU: the next row's loads are issued before this
+    // row's sums, barrier and stores (as in the RMSNorm backward).
+    LnBwdRow<S, VEC, ITERS> ta, tb;
+    ln_bwd_load_row(ta, a, 0, L, G);
+    for (int64_t step = 0; step < a.row_iters; step += 2) {
+      const bool has_b = step + 1 < a.row_iters;
+      if (has_b) ln_bwd_load_row(tb, a, step + 1, L, G);
+      ln_bwd_process_row(ta, a, step, w, accw, accb, red, L, G);
+      if (has_b) {
+        if (step + 2 < a.row_iters) ln_bwd_load_row(ta, a, step + 2, L, G);
+        ln_bwd_process_row(tb, a, step + 1, w, accw, accb, red, L, G);
       }
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      xv[i].keep_packed();
-      dv[i].keep_packed();
     }
-    s1 = wave_sum(s1);
-    s2 = wave_sum(s2);
-    if (a.wpr > 1) group_sum2(s1, s2, red, step, L.wave, L.group, a.wpr, L.lane);
-    const float c1 = s1 * a.inv_n;
-    const float c2 = s2 * a.inv_n;
+  } else {
+    // One row at a time.  This loop carries the same row work as
+    // ln_bwd_load_row + ln_bwd_process_row, written out in place: split into
+    // the two helpers it needs ~10 more registers and spills in the widest
+    // fp32 fallback instantiation (1-element vectors, 16 per lane).
+    for (int64_t step = 0; step < a.row_iters; ++step) {
+      const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
+      const bool active = row < a.M;
+      const int64_t off = active ? row * a.stride : 0;
+      const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? G.row_bytes : 0u);
+      const Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + off, active ? G.row_bytes : 0u);
+      const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + off, active ? G.row_bytes : 0u);
+
+      Pack<S, VEC> xv[ITERS];
+      Pack<S, VEC> dv[ITERS];
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) {
+        xv[i] = buf_load<S, VEC, kLnLoadXdy>(rx, voff + i * G.iter_bytes);
+        dv[i] = buf_load<S, VEC, kLnLoadXdy>(rd, voff + i * G.iter_bytes);
+      }
+      // mean and rstd of a missing row read as zero (out of the descriptors' range)
+      const uint32_t soff = active ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+      const float mean = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(G.mean, soff, 0, kDefault));
+      const float rstd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(G.rstd, soff, 0, kDefault));
+
+      // the two row sums: of x_hat * g and of g, with g = w * dy
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float xh = (xv[i].get(e) - mean) * rstd;
+          const float g = w[i][e] * dv[i].get(e);
+          s1 = fmaf(xh, g, s1);
+          s2 += g;
+        }
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) {
+        xv[i].keep_packed();
+        dv[i].keep_packed();
+      }
+      s1 = wave_sum(s1);
+      s2 = wave_sum(s2);
+      if (a.wpr > 1) group_sum2(s1, s2, red, step, L.wave, L.group, a.wpr, L.lane);
+      const float c1 = s1 * a.inv_n;
+      const float c2 = s2 * a.inv_n;
 
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      float o[VEC];
+      for (int i = 0; i < ITERS; ++i) {
+        float o[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float df = dv[i].get(e);
-        const float xh = (xv[i].get(e) - mean) * rstd;
-        o[e] = (w[i][e] * df - fmaf(xh, c1, c2)) * rstd;
-        accw[i][e] = fmaf(df, xh, accw[i][e]);
-        accb[i][e] += df;
+        for (int e = 0; e < VEC; ++e) {
+          const float df = dv[i].get(e);
+          const float xh = (xv[i].get(e) - mean) * rstd;
+          o[e] = (w[i][e] * df - fmaf(xh, c1, c2)) * rstd;
+          accw[i][e] = fmaf(df, xh, accw[i][e]);
+          accb[i][e] += df;
+        }
+        buf_store<S, VEC, kLnStoreDx>(round_pack<S, VEC>(o), rdx, voff + i * G.iter_bytes);
       }
-      buf_store<S, VEC, kLnStoreDx>(round_pack<S, VEC>(o), rdx, voff + i * iter_bytes);
     }
   }
 

@@ -76,6 +76,7 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
+  a.pipeline = bwd_pipelined(p, elsize(dtype));
   const int st = hip_status(launch_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;
   return st;

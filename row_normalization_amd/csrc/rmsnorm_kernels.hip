@@ -246,13 +246,32 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
     }
   }
 
-  // One row at a time.  (Measured on MI355X at 16384 x 8192 bf16: keeping a
-  // second row's loads in flight during a row's work, in 88 instead of ~64
-  // registers, made this pass about 6 % slower; the other waves on the CU
-  // already cover a row's reduction and barrier.)
-  for (int64_t step = 0; step < a.row_iters; ++step) {
-    bwd_load_row(ta, a, step, L, G);
-    bwd_process_row(ta, a, step, w, acc, red, L, G);
+  bool pipelined = false;
+  if constexpr (bwd_pipeline_fits(VEC, ITERS, sizeof(S))) pipelined = a.pipeline;
+  if (pipelined) {
+    // One workgroup per CU: the next row's loads are issued before this
+    // row's reduction, barrier and stores, so the memory system is not idle
+    // while they run.  Rows are still processed in order (the LDS slots of
+    // the row sums alternate by step).
+    BwdRow<S, VEC, ITERS> tb;
+    bwd_load_row(ta, a, 0, L, G);
+    for (int64_t step = 0; step < a.row_iters; step += 2) {
+      const bool has_b = step + 1 < a.row_iters;
+      if (has_b) bwd_load_row(tb, a, step + 1, L, G);
+      bwd_process_row(ta, a, step, w, acc, red, L, G);
+      if (has_b) {
+        if (step + 2 < a.row_iters) bwd_load_row(ta, a, step + 2, L, G);
+        bwd_process_row(tb, a, step + 1, w, acc, red, L, G);
+      }
+    }
+  } else {
+    // One row at a time: with two workgroups per CU the other workgroup's
+    // loads cover a row's reduction and barrier (pipelined, this pass ran
+    // 2-8 % slower at 16384 x 8192 and 32768 x 5120).
+    for (int64_t step = 0; step < a.row_iters; ++step) {
+      bwd_load_row(ta, a, step, L, G);
+      bwd_process_row(ta, a, step, w, acc, red, L, G);
+    }
   }
 
   // One partial row per workgroup: row groups are added in LDS in group order.

@@ -42,6 +42,8 @@ SMALL = [
     ("f16", 2, 3), ("f16", 31, 96), ("f16", 100, 1024), ("f16", 1030, 1536), ("f16", 7, 15872), ("f16", 5, 16384),
     # partly empty last waves (planner's choice)
     ("f16", 67, 7680), ("bf16", 45, 2560), ("f16", 300, 3584), ("f16", 29, 13312), ("f32", 23, 3328),
+    # one workgroup per CU, next row's loads in flight (3, 5, 3, 4 rows per workgroup)
+    ("f16", 600, 12288), ("bf16", 1100, 9216), ("f32", 513, 8192), ("f16", 1024, 10240),
 ]
 
 

@@ -94,6 +94,12 @@ SMALL = [
     ("bf16", 300, 3584, True, False),   # 4 x 2
     ("bf16", 129, 13312, False, False), # forward 7 x 4 (128 empty), backward 13 x 2
     ("f32", 23, 3328, False, False),    # fp32 7 x 2 rather than 13 x 1
+    # one workgroup per CU: the backward keeps the next row's loads in flight
+    # (odd and even numbers of rows per workgroup, in place)
+    ("bf16", 600, 12288, True, True),   # 3 rows per workgroup
+    ("f16", 1100, 9216, False, False),  # 5
+    ("f32", 513, 8192, False, True),    # 3, fp32 16 x 2
+    ("bf16", 1024, 10240, False, True), # 4
 ]
 
 
