@@ -16,8 +16,8 @@ constexpr int kMaxBlockWaves = 16; // 1024-thread workgroups at most
 // A row kernel processes rows in "row groups": `wpr` waves cooperate on one
 // row, `rpb` row groups share a workgroup (block = 64 * wpr * rpb threads).
 // Lane `l` of wave `w` in a group owns the VEC-element column vectors
-// v = (i * wpr + w) * 64 + l for i < iters; vectors at or past N / VEC are
-// masked.  Rows are assigned statically: at step k, group g of block b takes
+// v = (i * wpr + w) * 64 + l for i < iters (the RMSNorm backward:
+// v = (w * iters + i) * 64 + l); vectors at or past N / VEC are masked.  Rows are assigned statically: at step k, group g of block b takes
 // row (k * grid + b) * rpb + g, for k < row_iters.
 struct RowPlan {
   int vec;        // elements per vector load (16 bytes when alignment allows)

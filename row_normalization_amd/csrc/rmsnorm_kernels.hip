@@ -224,8 +224,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
   const Lane L(a.wpr);
   BwdGeom G;
-  G.voff = L.first_vec() * kPack;
-  G.iter_bytes = static_cast<uint32_t>(a.wpr) * kWave * kPack;
+  G.voff = static_cast<uint32_t>(L.template wave_vec<ITERS>(0)) * kPack;
+  G.iter_bytes = static_cast<uint32_t>(kWave) * kPack;
   G.row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
   G.rstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
 
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
   float* prow = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
   if (a.rpb == 1) {
     const Rsrc rp = make_rsrc(prow, static_cast<uint32_t>(a.N) * 4u);
-    const uint32_t voff32 = L.first_vec() * VEC * 4u;
-    const uint32_t iter32 = static_cast<uint32_t>(a.wpr) * kWave * VEC * 4u;
+    const uint32_t voff32 = static_cast<uint32_t>(L.template wave_vec<ITERS>(0)) * VEC * 4u;
+    const uint32_t iter32 = static_cast<uint32_t>(kWave) * VEC * 4u;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kDefault>(acc[i], rp, voff32 + i * iter32);
     return;
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
     if (L.group == g) {
 #pragma unroll
       for (int i = 0; i < ITERS; ++i) {
-        const int v = (i * a.wpr + L.wv) * kWave + L.lane;
+        const int v = L.template wave_vec<ITERS>(i);
         if (v < a.nvec) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
