@@ -414,6 +414,28 @@ def oracle_all_cores(w: wl.Workload, rows: int, seconds: float) -> dict:
                       f"{el:.1f} s"}
 
 
+def device_info() -> dict:
+    """Name, compute units, and the clocks and memory bus width the HIP runtime reports."""
+    import ctypes
+
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return out
+
+    def attr(code: int):
+        v = ctypes.c_int(0)
+        return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), code, 0) == 0 else None
+
+    # hipDeviceAttribute_t codes of ROCm 7's hip_runtime_api.h: ClockRate,
+    # MemoryBusWidth, MemoryClockRate (clocks in kHz)
+    sclk, bus, mclk = attr(5), attr(59), attr(60)
+    out.update({"sclk_mhz": sclk and sclk / 1000, "mem_clock_mhz": mclk and mclk / 1000, "mem_bus_bits": bus})
+    return out
+
+
 def cpu_baseline(w: wl.Workload, seconds: float, all_cores_seconds: float) -> dict:
     """The fp64 oracle (as it stands) on a sample of rows of the same workload."""
     rows = min(w.M, 1024)
@@ -469,7 +491,6 @@ def main():
     h = kernel_hash()
     traffic = traffic_from_profile(h)
     copy_gbps = copy_reference(256 << 20, 50)
-    props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -504,7 +525,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "rmsnorm_bwd_rows_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": b["bwd_rows"], "kernel_sha": h},
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": device_info(),
     }
     del path
     torch.cuda.empty_cache()
