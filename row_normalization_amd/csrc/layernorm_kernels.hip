@@ -41,7 +41,8 @@ namespace rmsn {
 namespace {
 using namespace dev;
 
-// Streamed operands are touched once per pass: nontemporal, as for RMSNorm.
+// Streamed operands are touched once per pass: nontemporal loads and
+// nontemporal device-scope stores, as for RMSNorm.
 constexpr int kLnLoadX = kNontemporal;
 constexpr int kLnStoreY = kStreamStore;
 constexpr int kLnLoadXdy = kNontemporal;

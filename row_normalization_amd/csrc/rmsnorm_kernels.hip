@@ -31,9 +31,11 @@
 //  - The backward is a persistent grid: each workgroup owns a fixed set of
 //    rows, keeps the weight and its dgamma column partials in registers
 //    across them, and writes one fp32 partial row at the end (row groups of
-//    the workgroup are combined in LDS in a fixed order).  A second small kernel sums the
-//    partial rows per column in a fixed order.  No atomics touch data, so
-//    every result is bitwise reproducible.
+//    the workgroup are combined in LDS in a fixed order).  Where one
+//    workgroup fills its CU, it issues the next row's loads before working
+//    on a row.  A second small kernel sums the partial rows per column in a
+//    fixed order.  No atomics touch data, so every result is bitwise
+//    reproducible.
 //  - dx may be written over dy: each lane reads its own dy elements before it
 //    writes the same elements of dx, and no other lane touches them.
 #include <hip/hip_runtime.h>
