@@ -1,0 +1,67 @@
+"""Seeded random shapes, strides, offsets and flags for both norms against the oracles.
+
+The cases are drawn once from fixed seeds, so a failure names a reproducible
+case: M log-uniform in [1, 3000], N alternately log-uniform in [1, 16384] and
+uniform in [1024, 16384], with M * N <= 3e6; fp32 / bf16 / fp16; row stride
+N + pad with pad in {0, 1, 8, 64, 333}; a base offset of 0, 1 or 3 elements
+(which forces the narrower vector widths); and at random the Gemma weight,
+dx written over dy, and the split (row pass + reduction) or fused backward.  The tolerances are
+those of ``tests.parity`` and ``tests.parity_ln``.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.parity import Run, compare_with_oracle
+from tests.parity_ln import LnRun, compare_ln_with_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(seed: int, n: int):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < n:
+        if len(out) % 2:
+            N = int(rng.integers(1024, 16385))
+        else:
+            N = max(1, min(16384, int(np.exp(rng.uniform(0.0, np.log(16384.0))))))
+        M = max(1, int(np.exp(rng.uniform(0.0, np.log(3000.0)))))
+        if M * N > 3_000_000:
+            continue
+        dtype = str(rng.choice(["f32", "bf16", "f16"]))
+        pad = int(rng.choice([0, 0, 1, 8, 64, 333]))
+        offset = int(rng.choice([0, 0, 1, 3]))
+        gemma, in_place, split = (bool(v) for v in rng.integers(0, 2, size=3))
+        out.append((dtype, M, N, pad, offset, gemma, in_place, split))
+    return out
+
+
+RMS_CASES = _cases(20261202, 24)
+LN_CASES = _cases(1151, 16)
+
+
+def _id(c):
+    dtype, M, N, pad, offset, gemma, in_place, split = c
+    return f"{dtype}-{M}x{N}-pad{pad}-off{offset}" + ("-gemma" if gemma else "") + ("-inplace" if in_place else "") + (
+        "-split" if split else "-fused")
+
+
+@pytest.mark.parametrize("case", RMS_CASES, ids=[_id(c) for c in RMS_CASES])
+def test_rmsnorm_random_case(case):
+    dtype, M, N, pad, offset, gemma, in_place, split = case
+    print("case:", _id(case), flush=True)
+    base = wl.C3 if gemma else wl.C2
+    w = base.scaled(M=M, N=N, dtype=dtype, gemma=gemma, dx_in_place=in_place, seed=M * 7919 + N)
+    if dtype == "f32":
+        w = w.scaled(dy=("normal", 0.0, 1.0))
+    compare_with_oracle(Run(w, row_stride=N + pad, offset=offset, split_bwd=split))
+
+
+@pytest.mark.parametrize("case", LN_CASES, ids=[_id(c) for c in LN_CASES])
+def test_layernorm_random_case(case):
+    dtype, M, N, pad, offset, _, in_place, split = case
+    print("case:", _id(case), flush=True)
+    w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
+                    dy=wl.LN1.dy, eps=1e-5, seed=M * 104729 + N)
+    compare_ln_with_oracle(LnRun(w, row_stride=N + pad, offset=offset, split_bwd=split, in_place=in_place))
