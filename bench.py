@@ -55,7 +55,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c3", choices=sorted(wl.RMS_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -236,10 +236,28 @@ def layernorm_sweep(steps: int, ns=None) -> dict:
             "median_bwd_gbps_page_formula": round(med("bwd_gbps_page_formula"), 1), "points": points}
 
 
+# Untimed work before each per-launch measurement.  On MI355X a new stream of
+# launches runs up to ~15 % slower for its first ~10 ms and then settles (seen
+# in rocprofv3 traces of 150 back-to-back SwiGLU forwards: ~150 us, rising to
+# ~176 us around 6-9 ms in, back to ~152 us from ~15 ms on), so each
+# measurement starts after at least this much work.
+WARM_SECONDS = 0.025
+
+
+def warm_up(fn, seconds: float = WARM_SECONDS, batch: int = 3) -> None:
+    """Run fn() in batches until `seconds` of (synchronised) wall time have passed."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def time_launches(fn, steps: int) -> float:
     """Mean seconds per launch of fn() over `steps` launches bracketed by events."""
-    for _ in range(3):
-        fn()
+    warm_up(fn)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record()
