@@ -23,18 +23,12 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family:
 // 32-bit data format; the range check is then offset against the byte count.
 constexpr int kRsrcWord3 = 0x00020000;
-// Cache-policy operand of buffer instructions (gfx950): bit 1 = nt
-// (nontemporal: streamed, not kept), bit 4 = sc1 (device scope).
+// Cache-policy operand of buffer instructions: 0 = default, 2 = nontemporal
+// (streamed, not kept).  (Measured on MI355X: adding the device-scope bit to
+// the row kernels' nontemporal stores, so they are written through L2, made
+// them 0.2-1.9 % slower in interleaved comparisons.)
 constexpr int kDefault = 0;
 constexpr int kNontemporal = 2;
-constexpr int kDeviceScope = 16;
-// Row outputs of the normalisation kernels: nontemporal at device scope, so
-// they are written through rather than left dirty in L2.  Measured on MI355X:
-// RMSNorm 16384 x 8192 bf16 forward and backward ~1 % faster cold and 0.3 %
-// back to back than nontemporal alone, LayerNorm's backward 1-6 % at M =
-// 4096; device scope without nt 35 % slower.  The elementwise kernels showed
-// no consistent difference and keep plain nontemporal stores.
-constexpr int kStreamStore = kNontemporal | kDeviceScope;
 
 // A descriptor for `bytes` bytes at `base`; accesses at or past `bytes` read
 // zero and write nothing.

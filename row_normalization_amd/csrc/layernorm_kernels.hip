@@ -41,12 +41,11 @@ namespace rmsn {
 namespace {
 using namespace dev;
 
-// Streamed operands are touched once per pass: nontemporal loads and
-// nontemporal device-scope stores, as for RMSNorm.
+// Streamed operands are touched once per pass: nontemporal, as for RMSNorm.
 constexpr int kLnLoadX = kNontemporal;
-constexpr int kLnStoreY = kStreamStore;
+constexpr int kLnStoreY = kNontemporal;
 constexpr int kLnLoadXdy = kNontemporal;
-constexpr int kLnStoreDx = kStreamStore;
+constexpr int kLnStoreDx = kNontemporal;
 
 // ---------------------------------------------------------------------------
 // Forward.  Grid as for the RMSNorm forward (row groups, or persistent where

@@ -53,17 +53,16 @@ using namespace dev;
 // ---------------------------------------------------------------------------
 // Cache policy of the streamed row operands: every byte of x, dy, y and dx is
 // touched once per pass, so all of them use the nontemporal forms, which do
-// not allocate in L2 or the 256 MB Infinity Cache (the stores also at device
-// scope, written through; see kStreamStore).  Measured on MI355X at
+// not allocate in L2 or the 256 MB Infinity Cache.  Measured on MI355X at
 // 16384 x 8192 bf16: an allocating x load in the forward loses a third of
 // the forward's bandwidth when the cache holds dirty lines (each allocation
 // then costs a write-back), and only pays off when the backward of the same
 // rows runs right after the forward and finds x still cached.
 // ---------------------------------------------------------------------------
 constexpr int kFwdLoadX = kNontemporal;
-constexpr int kFwdStoreY = kStreamStore;
+constexpr int kFwdStoreY = kNontemporal;
 constexpr int kBwdLoadXdy = kNontemporal;
-constexpr int kBwdStoreDx = kStreamStore;
+constexpr int kBwdStoreDx = kNontemporal;
 
 // ---------------------------------------------------------------------------
 // Forward: y = x * r * w, rstd = r.
