@@ -53,10 +53,11 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="c3", choices=sorted(wl.RMS_WORKLOADS))
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (this benchmark runs on one)")
+    ap.add_argument("--steps", type=int, default=200, help="timed fwd + bwd steps")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before them")
+    ap.add_argument("--workload", default="c3", choices=sorted(wl.RMS_WORKLOADS),
+                    help="RMSNorm workload: " + "; ".join(f"{k} = {v.name}" for k, v in sorted(wl.RMS_WORKLOADS.items())))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--cpu-all-cores-seconds", type=float, default=8.0,
