@@ -136,6 +136,23 @@ def _same_layout(ref: torch.Tensor, other: torch.Tensor, name: str, stride: int)
         raise ValueError(f"{name} must have contiguous rows")
 
 
+def _vec(t, n: int, dtype, name: str) -> None:
+    """A per-column (or per-row) vector: n elements of `dtype`, adjacent in memory."""
+    if t.dtype != dtype or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} elements")
+
+
+def _scratch_bytes(t, name: str, need_elems: int = 0) -> int:
+    """Bytes of a contiguous scratch tensor (at least `need_elems` fp32 elements)."""
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if need_elems and (t.dtype != torch.float32 or t.numel() < need_elems):
+        raise ValueError(f"{name} must be float32 with at least {need_elems} elements")
+    return t.numel() * t.element_size()
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -159,8 +176,8 @@ def rmsnorm_fwd(x, gamma, y, rstd, eps: float = 1e-6, gemma: bool = False, round
     _gpu(x, gamma, y, rstd)
     M, N, stride = _rows(x, "x")
     _same_layout(x, y, "y", stride)
-    if rstd.dtype != torch.float32 or rstd.numel() != M or (M > 1 and rstd.stride(0) != 1):
-        raise ValueError("rstd must be a contiguous float32 tensor of M elements")
+    _vec(gamma, N, x.dtype, "gamma")
+    _vec(rstd, M, torch.float32, "rstd")
     st = lib().rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, stride, float(eps), _dtype_code(x),
                            _flags(gemma, round_normed), _stream(stream))
     _check(st, "rmsnorm_fwd")
@@ -179,8 +196,8 @@ def _bwd_checks(x, gamma, dy, rstd, dx):
     M, N, stride = _rows(x, "x")
     _same_layout(x, dy, "dy", stride)
     _same_layout(x, dx, "dx", stride)
-    if rstd.dtype != torch.float32 or rstd.numel() != M:
-        raise ValueError("rstd must be float32 with M elements")
+    _vec(gamma, N, x.dtype, "gamma")
+    _vec(rstd, M, torch.float32, "rstd")
     return M, N, stride
 
 
@@ -188,9 +205,10 @@ def rmsnorm_bwd_rows(x, gamma, dy, rstd, dx, workspace, gemma: bool = False, str
     """dx (may be dy itself) and per-workgroup dgamma partial rows; returns the partial-row count."""
     M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
     _gpu(workspace)
+    wbytes = _scratch_bytes(workspace, "workspace")
     rows = _c_i64(0)
     st = lib().rmsnorm_bwd_rows(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), M, N, stride, _dtype_code(x),
+                                wbytes, M, N, stride, _dtype_code(x),
                                 _flags(gemma), ctypes.byref(rows), _stream(stream))
     _check(st, "rmsnorm_bwd_rows")
     return int(rows.value)
@@ -199,10 +217,9 @@ def rmsnorm_bwd_rows(x, gamma, dy, rstd, dx, workspace, gemma: bool = False, str
 def rmsnorm_dgamma_reduce(partials, rows: int, N: int, dgamma, stream=None) -> None:
     """dgamma[j] = sum of the first ``rows`` rows of the [rows, N] fp32 partials."""
     _gpu(partials, dgamma)
-    if dgamma.dtype != torch.float32 or dgamma.numel() != N:
-        raise ValueError("dgamma must be float32 with N elements")
-    if partials is not None and partials.dtype != torch.float32:
-        raise ValueError("partials must be float32")
+    _vec(dgamma, N, torch.float32, "dgamma")
+    if rows > 0:
+        _scratch_bytes(partials, "partials", int(rows) * int(N))
     st = lib().rmsnorm_dgamma_reduce(_ptr(partials), int(rows), int(N), _ptr(dgamma), _stream(stream))
     _check(st, "rmsnorm_dgamma_reduce")
 
@@ -211,9 +228,8 @@ def rmsnorm_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, gemma: bool = False, 
     """Full backward: dx (may be dy itself) and dgamma (fp32, overwritten)."""
     M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
     _gpu(dgamma, workspace)
-    if dgamma.dtype != torch.float32 or dgamma.numel() != N:
-        raise ValueError("dgamma must be float32 with N elements")
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _vec(dgamma, N, torch.float32, "dgamma")
+    wbytes = _scratch_bytes(workspace, "workspace")
     st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
                            wbytes, M, N, stride, _dtype_code(x), _flags(gemma), _stream(stream))
     _check(st, "rmsnorm_bwd")
@@ -233,9 +249,8 @@ def layernorm_fwd(x, weight, bias, y, mean, rstd, eps: float = 1e-5, stream=None
     _gpu(x, weight, bias, y, mean, rstd)
     M, N, stride = _rows(x, "x")
     _same_layout(x, y, "y", stride)
-    for t, name in ((weight, "weight"), (bias, "bias")):
-        if t.dtype != x.dtype or t.numel() != N:
-            raise ValueError(f"{name} must have x's dtype and N elements")
+    _vec(weight, N, x.dtype, "weight")
+    _vec(bias, N, x.dtype, "bias")
     _vec_f32(mean, M, "mean")
     _vec_f32(rstd, M, "rstd")
     st = lib().layernorm_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), _ptr(mean), _ptr(rstd), M, N, stride,
@@ -256,8 +271,7 @@ def _ln_bwd_checks(x, weight, dy, mean, rstd, dx):
     M, N, stride = _rows(x, "x")
     _same_layout(x, dy, "dy", stride)
     _same_layout(x, dx, "dx", stride)
-    if weight.dtype != x.dtype or weight.numel() != N:
-        raise ValueError("weight must have x's dtype and N elements")
+    _vec(weight, N, x.dtype, "weight")
     _vec_f32(mean, M, "mean")
     _vec_f32(rstd, M, "rstd")
     return M, N, stride
@@ -268,9 +282,10 @@ def layernorm_bwd_rows(x, weight, dy, mean, rstd, dx, workspace, stream=None) ->
     partial-row count (dw partials in rows [0, P), db partials in rows [P, 2P))."""
     M, N, stride = _ln_bwd_checks(x, weight, dy, mean, rstd, dx)
     _gpu(workspace)
+    wbytes = _scratch_bytes(workspace, "workspace")
     rows = _c_i64(0)
     st = lib().layernorm_bwd_rows(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), M, N, stride, _dtype_code(x),
+                                  wbytes, M, N, stride, _dtype_code(x),
                                   ctypes.byref(rows), _stream(stream))
     _check(st, "layernorm_bwd_rows")
     return int(rows.value)
@@ -281,8 +296,8 @@ def layernorm_dwdb_reduce(partials, rows: int, N: int, dw, db, stream=None) -> N
     _gpu(partials, dw, db)
     _vec_f32(dw, N, "dw")
     _vec_f32(db, N, "db")
-    if partials is not None and partials.dtype != torch.float32:
-        raise ValueError("partials must be float32")
+    if rows > 0:
+        _scratch_bytes(partials, "partials", 2 * int(rows) * int(N))
     st = lib().layernorm_dwdb_reduce(_ptr(partials), int(rows), int(N), _ptr(dw), _ptr(db), _stream(stream))
     _check(st, "layernorm_dwdb_reduce")
 
@@ -293,7 +308,7 @@ def layernorm_bwd(x, weight, dy, mean, rstd, dx, dw, db, workspace, stream=None)
     _gpu(dw, db, workspace)
     _vec_f32(dw, N, "dw")
     _vec_f32(db, N, "db")
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wbytes = _scratch_bytes(workspace, "workspace")
     st = lib().layernorm_bwd(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dw), _ptr(db),
                              _ptr(workspace), wbytes, M, N, stride, _dtype_code(x), _stream(stream))
     _check(st, "layernorm_bwd")

@@ -36,11 +36,14 @@ CALLS = {"forward": 0, "backward": 0, "ln_forward": 0, "ln_backward": 0, "rope_f
 
 
 def _rows(t: torch.Tensor) -> torch.Tensor:
-    """[..., N] -> [M, N] view with contiguous rows (a copy only if the last dim is strided)."""
+    """[..., N] -> dense [M, N] rows (a copy only if t's rows are strided or spaced).
+
+    The outputs the adapters allocate are dense, and the C ABI takes one row
+    stride for all row operands, so the input rows must be dense too."""
     if t.dim() == 0:
         raise ValueError("RMSNorm needs at least one dimension")
     t2 = t.reshape(-1, t.shape[-1])
-    if t2.shape[1] > 1 and t2.stride(1) != 1:
+    if (t2.shape[1] > 1 and t2.stride(1) != 1) or (t2.shape[0] > 1 and t2.stride(0) != t2.shape[1]):
         t2 = t2.contiguous()
     return t2
 
@@ -65,12 +68,9 @@ class RMSNormFunction(torch.autograd.Function):
     def backward(ctx, dy: torch.Tensor):
         x2, gamma, rstd = ctx.saved_tensors
         M, N = x2.shape
-        # the C ABI takes one row stride for x, dy and dx: use dense rows
-        # (dy.contiguous() as on the tutorial; x only needs a copy if the
-        # caller's x was a strided view)
+        # the C ABI takes one row stride for x, dy and dx: dense rows (x2 was
+        # made dense in the forward; dy.contiguous() as on the tutorial)
         dy2 = dy.reshape(M, N).contiguous()
-        if M > 1 and x2.stride(0) != N:
-            x2 = x2.contiguous()
         dx = torch.empty_like(dy2)
         dgamma = torch.empty(N, dtype=torch.float32, device=dy.device)
         ws_bytes = rmsnorm_bwd_workspace_bytes(M, N, x2.dtype)
@@ -132,8 +132,6 @@ class LayerNormFunction(torch.autograd.Function):
         x2, weight, bias, mean, rstd = ctx.saved_tensors
         M, N = x2.shape
         dy2 = dy.reshape(M, N).contiguous()
-        if M > 1 and x2.stride(0) != N:
-            x2 = x2.contiguous()
         dx = torch.empty_like(dy2)
         dw = torch.empty(N, dtype=torch.float32, device=dy.device)
         db = torch.empty(N, dtype=torch.float32, device=dy.device)

@@ -7,6 +7,10 @@
   in dx, so a NaN or an infinity planted in one row of x leaves every other
   row's y, r and dx bit-identical to the run without it (the weight gradient
   sums over rows and does take the non-finite contribution).
+* The Python binding rejects per-column vectors, scratch and partials of the
+  wrong size, dtype or layout before anything is launched.
+* The autograd adapters accept rows spaced apart (a column slice of a wider
+  buffer) and give the dense copy's results and gradients.
 """
 import pytest
 import torch
@@ -101,3 +105,64 @@ def test_non_finite_row_stays_in_its_row(norm, bad):
         assert torch.equal(dirty[k][keep], clean[k][keep]), f"{k}: rows other than the planted one changed"
         assert not torch.isfinite(dirty[k][bad_row].float()).all(), f"{k}: the planted row shows no non-finite value"
     assert torch.equal(dirty["rstd"][keep], clean["rstd"][keep])
+
+
+def test_binding_rejects_malformed_vectors_and_scratch():
+    """The Python binding checks what the C ABI cannot (sizes and layouts of the
+    per-column vectors, the scratch and the partials it is handed) and raises
+    before anything is launched."""
+    w = wl.C2.scaled(M=64, N=1024)
+    _case(w.name, "malformed arguments")
+    b = _rms_buffers(w)
+    ln = _ln_buffers(wl.LN1.scaled(M=64, N=1024))
+    y0 = b["y"].fill_(3.0).clone()
+    bad = {
+        "gamma too short": dict(g=b["g"][:-1]),
+        "gamma of another dtype": dict(g=b["g"].float()),
+        "strided gamma": dict(g=torch.cat([b["g"], b["g"]])[::2]),
+        "strided rstd": dict(rstd=torch.empty(2 * w.M, dtype=torch.float32, device="cuda")[::2]),
+    }
+    for what, repl in bad.items():
+        args = {**b, **repl}
+        with pytest.raises(ValueError):
+            rn.rmsnorm_fwd(args["x"], args["g"], args["y"], args["rstd"], eps=w.eps)
+        with pytest.raises(ValueError):
+            rn.rmsnorm_bwd(args["x"], args["g"], args["dy"], args["rstd"], args["dx"], args["dg"], args["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(b["y"], y0), "a rejected call wrote y"
+    with pytest.raises(ValueError):  # scratch given as a strided view
+        big = torch.empty(2 * b["ws"].numel(), dtype=torch.float32, device="cuda")
+        rn.rmsnorm_bwd(b["x"], b["g"], b["dy"], b["rstd"], b["dx"], b["dg"], big[::2])
+    with pytest.raises(ValueError):  # fewer partials than rows * N
+        rn.rmsnorm_dgamma_reduce(b["ws"][:100], 8, w.N, b["dg"])
+    with pytest.raises(ValueError):
+        rn.layernorm_fwd(ln["x"], ln["w"][:-1], ln["b"], ln["y"], ln["mean"], ln["rstd"])
+    with pytest.raises(ValueError):
+        rn.layernorm_fwd(ln["x"], ln["w"], torch.cat([ln["b"], ln["b"]])[::2], ln["y"], ln["mean"], ln["rstd"])
+    with pytest.raises(ValueError):
+        rn.layernorm_dwdb_reduce(ln["ws"][:100], 8, 1024, ln["dw"], ln["db"])
+
+
+def test_adapter_accepts_rows_with_a_row_stride():
+    """x given to the autograd adapters as a column slice of a wider buffer
+    (rows spaced apart) gives the same results as the dense copy."""
+    w = wl.C2.scaled(M=96, N=1000)
+    _case(w.name, "adapter on a strided view")
+    t = wl.make_inputs(w)
+    wide = torch.zeros(w.M, w.N + 40, dtype=t["x"].dtype, device="cuda")
+    wide[:, :w.N] = t["x"].cuda()
+    xv = wide[:, :w.N]
+    xd = t["x"].cuda()
+    g = t["gamma"].cuda()
+    dy = t["dy"].cuda()
+    assert torch.equal(rn.rmsnorm(xv, g, eps=w.eps), rn.rmsnorm(xd, g, eps=w.eps))
+    ln_w, ln_b = torch.rand(w.N, device="cuda").to(t["x"].dtype), torch.rand(w.N, device="cuda").to(t["x"].dtype)
+    assert torch.equal(rn.layernorm(xv, (w.N,), ln_w, ln_b), rn.layernorm(xd, (w.N,), ln_w, ln_b))
+    # gradients through the strided view
+    base = wide.clone().requires_grad_(True)
+    y = rn.rmsnorm(base[:, :w.N], g, eps=w.eps)
+    y.backward(dy)
+    ref = xd.clone().requires_grad_(True)
+    rn.rmsnorm(ref, g, eps=w.eps).backward(dy)
+    assert torch.equal(base.grad[:, :w.N], ref.grad)
+    assert torch.all(base.grad[:, w.N:] == 0)
