@@ -21,6 +21,11 @@ any leading shape are flattened to rows of the last dimension, which must be
 contiguous.  The weight gradient is accumulated in fp32 by the library and
 cast to gamma's dtype here, because autograd requires a gradient of the
 parameter's own dtype (``rmsnorm_bwd`` gives the fp32 values directly).
+
+The functional forms are excluded from ``torch.compile`` tracing
+(``torch.compiler.disable``), as the walkthrough does for its kernels: the
+calls go through ctypes into the library, which Dynamo cannot trace, so a
+compiled model runs them eagerly between its compiled regions.
 """
 from __future__ import annotations
 
@@ -80,6 +85,7 @@ class RMSNormFunction(torch.autograd.Function):
         return dx.view(ctx.x_shape), dgamma.to(gamma.dtype), None, None, None
 
 
+@torch.compiler.disable
 def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, gemma: bool = False,
             round_normed: bool = False) -> torch.Tensor:
     """Functional form: RMSNorm over the last dimension of x.
@@ -142,6 +148,7 @@ class LayerNormFunction(torch.autograd.Function):
         return dx.view(ctx.x_shape), None, dw.to(weight.dtype), db.to(bias.dtype), None
 
 
+@torch.compiler.disable
 def layernorm(x: torch.Tensor, normalized_shape, weight: torch.Tensor, bias: torch.Tensor,
               eps: float = 1e-5) -> torch.Tensor:
     """Functional form with the signature of ``torch.nn.functional.layer_norm``
@@ -187,6 +194,7 @@ class RoPEFunction(torch.autograd.Function):
         return dq, None, None, None, None
 
 
+@torch.compiler.disable
 def rope_embedding(q: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, positions=None, seq_len=None):
     """In-place rotary embedding of q [tokens, heads, head_dim] (see RoPEFunction)."""
     return RoPEFunction.apply(q, cos, sin, positions, seq_len)
@@ -218,6 +226,7 @@ class SwiGLUFunction(torch.autograd.Function):
         return de.view(ctx.shape), dg.view(ctx.shape)
 
 
+@torch.compiler.disable
 def swiglu(e: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
     """Elementwise SwiGLU h = silu(e) * g with autograd (see SwiGLUFunction)."""
     return SwiGLUFunction.apply(e, g)

@@ -103,3 +103,24 @@ def test_training_matches_cpu_reference():
     for (n1, p1), (n2, p2) in zip(kernel_net.named_parameters(), ref_net.named_parameters()):
         diff = (p1.detach().double().cpu() - p2.detach()).abs().max().item()
         assert diff < 1e-4, (n1, diff)
+
+
+def test_adapters_inside_a_compiled_function():
+    """A torch.compile'd function (Dynamo, eager backend) that calls the
+    adapters runs them through the library (they are excluded from tracing)
+    and matches the uncompiled function bit for bit."""
+    torch.manual_seed(1)
+    norm = rn.RMSNorm(256, eps=1e-6, dtype=torch.float32, device="cuda")
+    lin = torch.nn.Linear(256, 256, device="cuda")
+    lw, lb = torch.rand(256, device="cuda"), torch.rand(256, device="cuda")
+
+    def f(x):
+        return rn.layernorm(lin(norm(x)), (256,), lw, lb).square().sum()
+
+    x = torch.randn(8, 256, device="cuda")
+    eager = f(x)
+    before = dict(rn.CALLS)
+    compiled = torch.compile(f, backend="eager")(x)
+    torch.cuda.synchronize()
+    assert rn.CALLS["forward"] == before["forward"] + 1 and rn.CALLS["ln_forward"] == before["ln_forward"] + 1
+    assert torch.equal(compiled, eager)
