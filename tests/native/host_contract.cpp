@@ -1,0 +1,235 @@
+// The host side of every entry point, built without any device code: the
+// launchers are replaced by stubs that check what the host hands the kernels
+// (launch plan, kernel arguments, descriptor ranges, LDS size, grid limits)
+// and launch nothing.  The driver calls every entry point over a grid of
+// shapes, dtypes, row strides, flags, in-place and misaligned cases with
+// valid (never dereferenced) device addresses: each such call must return
+// RMSNORM_OK and hand the kernels a consistent plan.  Built and run by
+// tests/test_host_contract.py with AddressSanitizer and UndefinedBehavior-
+// Sanitizer, which also watch the validation arithmetic itself.  Prints one
+// summary line and exits non-zero on any failure.
+#include <cstdint>
+#include <cstdio>
+#include <initializer_list>
+
+#include "host_plan.h"
+#include "launch.h"
+#include "layernorm.h"
+#include "rmsnorm.h"
+#include "rope.h"
+#include "swiglu.h"
+
+namespace {
+long g_checks = 0, g_bad = 0, g_launches = 0;
+
+void expect(bool ok, const char* what, long long a = 0, long long b = 0) {
+  ++g_checks;
+  if (!ok && g_bad++ < 20) std::printf("failed: %s (%lld, %lld)\n", what, a, b);
+}
+
+int elsize_of(int dtype) { return dtype == 0 ? 4 : 2; }
+bool in_iters_set(int it) {
+  for (int v : rmsn::kItersSet)
+    if (v == it) return true;
+  return false;
+}
+
+// What every row-kernel launch must satisfy.
+void check_row_plan(const rmsn::RowPlan& p, rmsn::RowOp op, int dtype, int64_t M, int64_t stride, int32_t N,
+                    int32_t nvec, int32_t wpr, int32_t rpb, int64_t row_iters) {
+  using namespace rmsn;
+  const int es = elsize_of(dtype);
+  const bool bwd = op == RowOp::kRmsBwd || op == RowOp::kLnBwd;
+  expect(p.vec == 1 || p.vec == 2 || p.vec == 4 || p.vec == 8, "vector width", p.vec);
+  expect(p.vec * es <= 16, "vector bytes", p.vec * es);
+  expect(N % p.vec == 0 && stride % p.vec == 0, "width divides N and the stride", N, stride);
+  expect(int64_t(nvec) * p.vec == N, "nvec * vec == N", nvec, N);
+  expect(in_iters_set(p.iters), "iters compiled", p.iters);
+  expect(p.vec * p.iters <= lane_elems_cap(op, es), "register model", p.vec * p.iters);
+  expect(p.wpr >= 1 && p.wpr <= kMaxBlockWaves && p.rpb >= 1 && p.threads() <= 1024, "workgroup shape", p.wpr,
+         p.rpb);
+  expect(int64_t(p.iters) * kWave * p.wpr * p.vec >= N, "row covered", N);
+  expect(p.grid >= 1 && p.grid <= (int64_t(1) << 31) - 1, "grid size", p.grid);
+  expect(p.grid * p.row_iters * p.rpb >= M, "rows covered", M);
+  expect(!bwd || p.grid <= kBwdGridMax, "backward grid", p.grid);
+  expect(wpr == p.wpr && rpb == p.rpb && row_iters == p.row_iters, "arguments match the plan");
+  expect(stride >= N, "stride", stride, N);
+  expect(int64_t(N) * es < (int64_t(1) << 31), "row descriptor range", N);
+  expect(M * 4 <= (int64_t(1) << 31), "per-row scalar descriptor range", M);
+}
+}  // namespace
+
+namespace rmsn {
+hipError_t launch_fwd(int dtype, const RowPlan& p, const FwdArgs& a, hipStream_t) {
+  ++g_launches;
+  check_row_plan(p, RowOp::kRmsFwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
+  expect(a.x && a.gamma && a.y && a.rstd, "forward pointers");
+  return hipSuccess;
+}
+hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStream_t) {
+  ++g_launches;
+  check_row_plan(p, RowOp::kRmsBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
+  expect(p.rpb == 1 || int64_t(a.N) * 4 <= 65536, "LDS combine size", a.N);
+  expect(!a.pipeline || (bwd_pipeline_fits(p.vec, p.iters, elsize_of(dtype)) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
+         "pipelined only where it fits and one workgroup fills the CU");
+  expect(p.grid <= partial_rows_bound(a.M), "partial rows within the workspace", p.grid);
+  return hipSuccess;
+}
+hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t) {
+  ++g_launches;
+  expect(vec == 1 || vec == 4, "reduce width", vec);
+  expect(tables == 1 || tables == 2, "tables", tables);
+  expect((tables == 2) == (a.dgamma2 != nullptr), "second output iff two tables");
+  expect(a.rows >= 0 && a.rows * a.N * 4 <= (int64_t(1) << 31), "partials descriptor range", a.rows, a.N);
+  expect(a.N % vec == 0, "reduce width divides N", a.N, vec);
+  return hipSuccess;
+}
+hipError_t launch_ln_fwd(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t) {
+  ++g_launches;
+  check_row_plan(p, RowOp::kLnFwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
+  return hipSuccess;
+}
+hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t) {
+  ++g_launches;
+  check_row_plan(p, RowOp::kLnBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
+  expect(p.rpb == 1 || int64_t(a.N) * 8 <= 65536, "LDS combine size", a.N);
+  expect(!a.pipeline || (bwd_pipeline_fits(p.vec, p.iters, elsize_of(dtype)) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
+         "pipelined only where it fits and one workgroup fills the CU");
+  return hipSuccess;
+}
+hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t) {
+  ++g_launches;
+  const int es = elsize_of(dtype);
+  expect(vec >= 1 && vec * es <= 16 && a.half % vec == 0, "rope width", vec, a.half);
+  expect(a.nvh * vec == a.half, "rope vectors per half");
+  expect(a.groups == (a.heads + kRopeGroup - 1) / kRopeGroup, "rope head groups");
+  expect(a.items == a.tokens * a.groups * a.nvh, "rope items");
+  expect((a.items + kEltThreads - 1) / kEltThreads <= (int64_t(1) << 31) - 1, "rope grid");
+  expect(a.table_rows * a.half * 4 < (int64_t(1) << 31), "table descriptor range");
+  expect(int64_t(a.heads) * a.half * 2 * es < (int64_t(1) << 31), "token descriptor range");
+  expect(a.sin_sign == 1.0f || a.sin_sign == -1.0f, "rope direction");
+  return hipSuccess;
+}
+static void check_swiglu(int dtype, int vec, const SwigluArgs& a) {
+  const int es = elsize_of(dtype);
+  expect(vec >= 1 && vec * es <= 16 && a.N % vec == 0, "swiglu width", vec, a.N);
+  expect(a.tiles == (a.N / vec + kSwigluUnroll * kEltThreads - 1) / (kSwigluUnroll * kEltThreads), "swiglu tiles");
+  expect(a.blocks == a.M * a.tiles, "swiglu blocks");
+  expect(a.last_row_elems >= 1 && a.last_row_elems <= a.N, "last row length", a.last_row_elems, a.N);
+  expect(a.stride >= a.N && int64_t(a.N) * es < (int64_t(1) << 31), "swiglu row range", a.N);
+}
+hipError_t launch_swiglu_fwd(int dtype, int vec, const SwigluArgs& a, hipStream_t) {
+  ++g_launches;
+  check_swiglu(dtype, vec, a);
+  return hipSuccess;
+}
+hipError_t launch_swiglu_bwd(int dtype, int vec, const SwigluArgs& a, hipStream_t) {
+  ++g_launches;
+  check_swiglu(dtype, vec, a);
+  expect(a.dh && a.df && a.de, "backward pointers");
+  return hipSuccess;
+}
+}  // namespace rmsn
+
+namespace {
+// Far-apart, 256-byte aligned device addresses (never dereferenced): slot k
+// lies at k * 2^46 bytes, more than any matrix the ABI accepts spans.
+char* slot(int k, int64_t misalign_bytes = 0) {
+  return reinterpret_cast<char*>((uintptr_t(1) << 46) * uintptr_t(k + 1) + uintptr_t(misalign_bytes));
+}
+
+void expect_ok(int st, const char* what, int64_t M, int64_t N) {
+  expect(st == RMSNORM_OK, what, M, N);
+  if (st != RMSNORM_OK && g_bad <= 20) std::printf("   status %d: %s\n", st, rmsnorm_status_string(st));
+}
+
+void norms(int64_t M, int64_t N, int64_t stride, int dtype, int64_t mis) {
+  const int es = elsize_of(dtype);
+  const int64_t off = mis * es;  // element-aligned, possibly not 16-byte aligned
+  size_t wbytes = 0, lwbytes = 0;
+  expect_ok(rmsnorm_bwd_workspace_bytes(M, N, dtype, &wbytes), "rms workspace query", M, N);
+  expect_ok(layernorm_bwd_workspace_bytes(M, N, dtype, &lwbytes), "ln workspace query", M, N);
+  const hipStream_t s = nullptr;
+  for (int flags : {0, int(RMSNORM_GEMMA), int(RMSNORM_GEMMA | RMSNORM_ROUND_NORMED)}) {
+    expect_ok(rmsnorm_fwd(slot(0, off), slot(1), slot(2, off), reinterpret_cast<float*>(slot(3)), M, N, stride, 1e-6f,
+                          dtype, flags, s),
+              "rmsnorm_fwd", M, N);
+    for (bool in_place : {false, true}) {
+      void* dy = slot(4, off);
+      void* dx = in_place ? dy : slot(5, off);
+      int64_t rows = -1;
+      expect_ok(rmsnorm_bwd_rows(slot(0, off), slot(1), dy, reinterpret_cast<const float*>(slot(3)), dx, slot(6),
+                                 wbytes, M, N, stride, dtype, flags & RMSNORM_GEMMA, &rows, s),
+                "rmsnorm_bwd_rows", M, N);
+      expect(rows >= 0 && rows <= rmsn::partial_rows_bound(M), "partial rows reported", rows, M);
+      expect_ok(rmsnorm_bwd(slot(0, off), slot(1), dy, reinterpret_cast<const float*>(slot(3)), dx,
+                            reinterpret_cast<float*>(slot(7)), slot(6), wbytes, M, N, stride, dtype,
+                            flags & RMSNORM_GEMMA, s),
+                "rmsnorm_bwd", M, N);
+    }
+  }
+  expect_ok(layernorm_fwd(slot(0, off), slot(1), slot(8), slot(2, off), reinterpret_cast<float*>(slot(3)),
+                          reinterpret_cast<float*>(slot(9)), M, N, stride, 1e-5f, dtype, s),
+            "layernorm_fwd", M, N);
+  for (bool in_place : {false, true}) {
+    void* dy = slot(4, off);
+    void* dx = in_place ? dy : slot(5, off);
+    int64_t rows = -1;
+    expect_ok(layernorm_bwd_rows(slot(0, off), slot(1), dy, reinterpret_cast<const float*>(slot(3)),
+                                 reinterpret_cast<const float*>(slot(9)), dx, slot(6), lwbytes, M, N, stride, dtype,
+                                 &rows, s),
+              "layernorm_bwd_rows", M, N);
+    expect_ok(layernorm_bwd(slot(0, off), slot(1), dy, reinterpret_cast<const float*>(slot(3)),
+                            reinterpret_cast<const float*>(slot(9)), dx, reinterpret_cast<float*>(slot(7)),
+                            reinterpret_cast<float*>(slot(10)), slot(6), lwbytes, M, N, stride, dtype, s),
+              "layernorm_bwd", M, N);
+  }
+}
+}  // namespace
+
+int main() {
+  const int64_t Ms[] = {0, 1, 7, 17, 300, 4096, 16384, 65537, int64_t(1) << 20, int64_t(1) << 29};
+  const int64_t Ns[] = {1, 2, 3, 8, 96, 257, 1000, 1024, 1536, 2560, 4096, 5120, 7680, 8192, 9216, 13312, 15872,
+                        16383, 16384};
+  for (int dtype = 0; dtype < 3; ++dtype)
+    for (int64_t M : Ms)
+      for (int64_t N : Ns)
+        for (int64_t pad : {0, 1, 8, 64})
+          for (int64_t mis : {0, 1}) norms(M, N, N + pad, dtype, mis);
+
+  // RoPE: heads x head_dim per token, dense or a view of a wider (fused) row
+  for (int dtype = 0; dtype < 3; ++dtype)
+    for (int64_t T : {int64_t(0), int64_t(1), int64_t(33), int64_t(8192), int64_t(1) << 22})
+      for (int64_t H : {1, 3, 32, 64})
+        for (int64_t D : {2, 6, 64, 128, 256, 1024})
+          for (int64_t extra : {int64_t(0), 2 * H * D}) {
+            const int64_t stride = H * D + extra;
+            for (bool with_positions : {false, true}) {
+              const int32_t* pos = with_positions ? reinterpret_cast<const int32_t*>(slot(3)) : nullptr;
+              expect_ok(rope_fwd(slot(0), T, H, D, stride, reinterpret_cast<const float*>(slot(1)),
+                                 reinterpret_cast<const float*>(slot(2)), 4096, pos, 2048, dtype, nullptr),
+                        "rope_fwd", T, H * D);
+              expect_ok(rope_bwd(slot(0), T, H, D, stride, reinterpret_cast<const float*>(slot(1)),
+                                 reinterpret_cast<const float*>(slot(2)), 4096, pos, 2048, dtype, nullptr),
+                        "rope_bwd", T, H * D);
+            }
+          }
+
+  // SwiGLU: dense (walked as flat rows) and strided, outputs separate or over the inputs
+  for (int dtype = 0; dtype < 3; ++dtype)
+    for (int64_t M : {int64_t(0), int64_t(1), int64_t(7), int64_t(11136), int64_t(1) << 20})
+      for (int64_t N : {int64_t(1), int64_t(3), int64_t(513), int64_t(14336), int64_t(70000), int64_t(1) << 26})
+        for (int64_t pad : {int64_t(0), int64_t(5)}) {
+          if (M * (N + pad) > (int64_t(1) << 40)) continue;
+          const int64_t stride = N + pad;
+          expect_ok(swiglu_fwd(slot(0), slot(1), slot(2), M, N, stride, dtype, nullptr), "swiglu_fwd", M, N);
+          expect_ok(swiglu_fwd(slot(0), slot(1), slot(0), M, N, stride, dtype, nullptr), "swiglu_fwd over e", M, N);
+          expect_ok(swiglu_bwd(slot(3), slot(0), slot(1), slot(4), slot(5), slot(6), M, N, stride, dtype, nullptr),
+                    "swiglu_bwd", M, N);
+          expect_ok(swiglu_bwd(slot(3), slot(0), slot(1), slot(3), slot(0), slot(1), M, N, stride, dtype, nullptr),
+                    "swiglu_bwd in place", M, N);
+        }
+
+  std::printf("%ld launches checked, %ld checks, %ld bad\n", g_launches, g_checks, g_bad);
+  return g_bad ? 1 : 0;
+}
