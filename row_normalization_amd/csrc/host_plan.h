@@ -38,6 +38,7 @@ constexpr int64_t kBwdGridMax = 1024;
 // dimension stays small (rows beyond it are taken in further steps).
 constexpr int64_t kFwdGridMax = 1 << 20;
 constexpr int64_t kFwdPersistentMinSteps = 8;
+constexpr int64_t kFwdPersistentMinWaves = 14;
 
 inline int elsize(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
 
@@ -154,17 +155,26 @@ inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int es, int lane_elems, 
   const int64_t groups = ceil_div(M, p.rpb);
   int64_t per_cu = 1;
   while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
-  // The forward is persistent only where that grid fills every CU with
-  // exactly kBwdResidentWaves waves and each workgroup then takes at least
-  // kFwdPersistentMinSteps row groups (its weight stays in registers across
-  // them; measured 2-4 % faster at 16384 x 8192 and 8192 x 16384, 7-9 % for
-  // LayerNorm at 4096 x 8192 and larger).  Elsewhere one workgroup per row
-  // group is faster: 5-wave rows at N = 5120 leave 10 waves per CU (8 %
-  // slower persistent at 32768 x 5120), and with 2-4 row groups per
-  // workgroup (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a
-  // workgroup queue behind each other (3-15 % slower).
-  const bool fwd_persistent = per_cu * p.wpr * p.rpb == kBwdResidentWaves &&
-                              groups >= kFwdPersistentMinSteps * kComputeUnits * per_cu;
+  // The forward is persistent where that grid fills every CU with
+  // kBwdResidentWaves waves, or with at least kFwdPersistentMinWaves waves
+  // whose lanes each carry four 16-byte vectors, and each workgroup then
+  // takes at least kFwdPersistentMinSteps row groups (its weights stay in
+  // registers across them).  Measured on MI355X: 2-4 % faster at 16384 x 8192
+  // and 8192 x 16384, 7-9 % for LayerNorm at 4096 x 8192 and larger; 7-wave
+  // rows of four vectors (N = 12800-14336 16-bit, fp32 N = 7168) 0.5-3.6 %
+  // faster for RMSNorm and 5-10 % for LayerNorm, which loads two weight
+  // vectors per workgroup.  Elsewhere one workgroup per row group is faster:
+  // with fewer waves per CU or two vectors per lane a persistent grid keeps
+  // too few loads in flight (5-wave rows at N = 5120, 10 waves per CU: 8-12 %
+  // slower; 7-wave rows of two vectors at N = 7168: 1-6 % slower; 6-wave rows
+  // of four: -3 ... +3 %), and with 2-4 row groups per workgroup
+  // (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a workgroup queue
+  // behind each other (3-15 % slower).
+  const int64_t cu_waves = per_cu * p.wpr * p.rpb;
+  const bool four_full_vectors = p.iters == 4 && p.vec * es == 16;
+  const bool fwd_persistent =
+      (cu_waves == kBwdResidentWaves || (cu_waves >= kFwdPersistentMinWaves && four_full_vectors)) &&
+      groups >= kFwdPersistentMinSteps * kComputeUnits * per_cu;
   const int64_t grid_cap = backward         ? std::min(kBwdGridMax, kComputeUnits * per_cu)
                            : fwd_persistent ? kComputeUnits * per_cu
                                             : kFwdGridMax;

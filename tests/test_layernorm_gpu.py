@@ -44,6 +44,8 @@ SMALL = [
     ("f16", 67, 7680), ("bf16", 45, 2560), ("f16", 300, 3584), ("f16", 29, 13312), ("f32", 23, 3328),
     # one workgroup per CU, next row's loads in flight (3, 5, 3, 4 rows per workgroup)
     ("f16", 600, 12288), ("bf16", 1100, 9216), ("f32", 513, 8192), ("f16", 1024, 10240),
+    # persistent forward with 7-wave rows of four vectors, ragged last row step
+    ("bf16", 4100, 14336),
 ]
 
 
@@ -55,7 +57,7 @@ def test_small_shapes(dtype, M, N):
     compare_ln_with_oracle(LnRun(w))
 
 
-@pytest.mark.parametrize("N", [1024, 8192, 15872])
+@pytest.mark.parametrize("N", [1024, 8192, 13312, 15872])
 def test_sweep_points(N):
     """Points of the chapter's bandwidth sweep (M = 4096, fp16) in full."""
     w = wl.ln_sweep(N)

@@ -100,6 +100,10 @@ SMALL = [
     ("f16", 1100, 9216, False, False),  # 5
     ("f32", 513, 8192, False, True),    # 3, fp32 16 x 2
     ("bf16", 1024, 10240, False, True), # 4
+    # persistent forward with 7-wave rows of four vectors; the last of its 9
+    # row steps holds rows for only some workgroups
+    ("f32", 4100, 7168, False, True),
+    ("bf16", 4097, 12800, True, False),
 ]
 
 
