@@ -27,7 +27,8 @@
  *              loads are range-checked by the hardware) and so writes zeros.
  * tokens == 0 is a no-op.  Errors (nothing is launched): RMSNORM_E_DTYPE,
  * RMSNORM_E_SHAPE (tokens < 0, heads < 1, head_dim odd or outside [2, 1024],
- * table_rows < 1, table_rows * head_dim / 2 > 2^29, tokens > RMSNORM_M_MAX,
+ * heads * head_dim > 2^24, table_rows < 1, table_rows * head_dim / 2 > 2^28,
+ * tokens > RMSNORM_M_MAX, token_stride * tokens beyond 2^60 elements,
  * seq_len outside [1, table_rows] without positions), RMSNORM_E_STRIDE
  * (token_stride < heads * head_dim), RMSNORM_E_NULL, RMSNORM_E_ALIGN,
  * RMSNORM_E_ALIAS (q overlaps a table or positions).

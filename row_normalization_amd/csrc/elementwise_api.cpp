@@ -3,6 +3,7 @@
 // points.  Validation is plain host arithmetic (no HIP call) and finishes
 // before anything is launched; on failure nothing is written.
 #include <cstdint>
+#include <limits>
 
 #include "host_plan.h"
 #include "launch.h"
@@ -26,11 +27,13 @@ int rope(void* q, int64_t tokens, int64_t heads, int64_t head_dim, int64_t token
          hipStream_t stream) {
   if (!valid_dtype(dtype)) return RMSNORM_E_DTYPE;
   if (tokens < 0 || tokens > RMSNORM_M_MAX || heads < 1 || head_dim < 2 || head_dim > kRopeHeadDimMax ||
-      head_dim % 2 || heads * head_dim > kRopeTokenElemsMax || table_rows < 1 ||
+      head_dim % 2 || heads > kRopeTokenElemsMax / head_dim || table_rows < 1 ||
       table_rows > kRopeTableMax / (head_dim / 2))
     return RMSNORM_E_SHAPE;
   if (!positions && (seq_len < 1 || seq_len > table_rows)) return RMSNORM_E_SHAPE;
   if (token_stride < heads * head_dim) return RMSNORM_E_STRIDE;
+  // byte offsets of every token must fit int64 (as for the row-wise ops)
+  if (tokens > 0 && token_stride > (std::numeric_limits<int64_t>::max() / 8) / tokens) return RMSNORM_E_SHAPE;
   if (tokens == 0) return RMSNORM_OK;
   if (!q || !cos || !sin) return RMSNORM_E_NULL;
   const int es = elsize(dtype);

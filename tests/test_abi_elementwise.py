@@ -38,6 +38,9 @@ def test_rope_rejections(L, fn):
     assert rope(L, fn, pos=None, seq=0) == E_SHAPE
     assert rope(L, fn, pos=None, seq=17) == E_SHAPE  # seq_len beyond the table
     assert rope(L, fn, stride=4 * 128 - 1) == E_STRIDE
+    assert rope(L, fn, H=(1 << 24) // 128 + 1) == E_SHAPE   # heads * head_dim > 2^24
+    assert rope(L, fn, H=1 << 62, stride=1 << 40) == E_SHAPE  # no overflow in heads * head_dim
+    assert rope(L, fn, stride=1 << 61) == E_SHAPE           # byte offsets beyond int64
     for kw in ("q", "cos", "sin"):
         assert rope(L, fn, **{kw: None}) == E_NULL, kw
     assert rope(L, fn, q=Q + 1) == E_ALIGN
