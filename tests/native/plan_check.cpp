@@ -44,10 +44,12 @@ int main() {
   const Pin pins[] = {
       {2, 8192, RowOp::kRmsFwd, 8, 2},   {2, 8192, RowOp::kRmsBwd, 8, 2},    // no waste
       {2, 7680, RowOp::kRmsFwd, 8, 2},   {2, 7680, RowOp::kLnBwd, 8, 2},     // not 15 x 1
-      {2, 2560, RowOp::kLnFwd, 3, 2},    {2, 4608, RowOp::kRmsBwd, 5, 2},    // not 5 x 1, 9 x 1
+      {2, 2560, RowOp::kLnFwd, 1, 5},    {2, 4608, RowOp::kRmsBwd, 5, 2},    // forward: not 3 x 2; not 5 x 1, 9 x 1
+      {2, 3072, RowOp::kLnFwd, 3, 2},    {2, 2560, RowOp::kLnBwd, 3, 2},     // three waves kept
       {2, 16384, RowOp::kRmsFwd, 8, 4},  {2, 16384, RowOp::kRmsBwd, 16, 2},  // forward rows of <= 8 waves
       {2, 13312, RowOp::kLnFwd, 7, 4},   {2, 13312, RowOp::kLnBwd, 13, 2},
-      {2, 1536, RowOp::kRmsFwd, 3, 1},                                        // 2 x 2 would waste a quarter
+      {2, 1536, RowOp::kRmsFwd, 1, 4},   {2, 1536, RowOp::kRmsBwd, 2, 2},    // not 3 x 1
+      {2, 1232, RowOp::kLnFwd, 1, 4},
       {4, 14848, RowOp::kRmsFwd, 12, 5}, {4, 7680, RowOp::kRmsFwd, 6, 5},    // fp32: least waste first
       {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
   };

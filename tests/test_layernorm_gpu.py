@@ -46,6 +46,8 @@ SMALL = [
     ("f16", 600, 12288), ("bf16", 1100, 9216), ("f32", 513, 8192), ("f16", 1024, 10240),
     # persistent forward with 7-wave rows of four vectors, ragged last row step
     ("bf16", 4100, 14336),
+    # forward rows of three waves' width run as one wave of 4 or 5 vectors
+    ("f16", 300, 1232), ("bf16", 129, 2504),
 ]
 
 

@@ -104,6 +104,10 @@ SMALL = [
     # row steps holds rows for only some workgroups
     ("f32", 4100, 7168, False, True),
     ("bf16", 4097, 12800, True, False),
+    # forward rows of three waves' width run as one wave of 4 or 5 vectors
+    # (the last vectors of the lane partly or wholly past N)
+    ("bf16", 700, 1232, False, True),
+    ("f16", 300, 2504, True, False),
 ]
 
 
