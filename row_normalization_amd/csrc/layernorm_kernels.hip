@@ -345,23 +345,13 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
   }
 
   // One dw and one db partial row per workgroup; row groups are added in LDS
-  // in group order.
+  // in group order, and the last group adds that sum to its own and writes
+  // the two partial rows (every group covers every column; lanes past the
+  // row's end store out of the descriptors' range).
   float* pw = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
   float* pb = a.partials + (static_cast<int64_t>(gridDim.x) + blockIdx.x) * a.N;
-  if (a.rpb == 1) {
-    const Rsrc rdw = make_rsrc(pw, static_cast<uint32_t>(a.N) * 4u);
-    const Rsrc rdb = make_rsrc(pb, static_cast<uint32_t>(a.N) * 4u);
-    const uint32_t voff32 = L.first_vec() * VEC * 4u;
-    const uint32_t iter32 = static_cast<uint32_t>(a.wpr) * kWave * VEC * 4u;
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      buf_store_f32<VEC, kDefault>(accw[i], rdw, voff32 + i * iter32);
-      buf_store_f32<VEC, kDefault>(accb[i], rdb, voff32 + i * iter32);
-    }
-    return;
-  }
-  for (int g = 0; g < a.rpb; ++g) {
-    __syncthreads();
+  for (int g = 0; g < a.rpb - 1; ++g) {
+    if (g > 0) __syncthreads();
     if (L.group == g) {
 #pragma unroll
       for (int i = 0; i < ITERS; ++i) {
@@ -397,10 +387,31 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
       }
     }
   }
-  __syncthreads();
-  for (int col = threadIdx.x; col < a.N; col += blockDim.x) {
-    pw[col] = comb[col];
-    pb[col] = comb[a.N + col];
+  if (a.rpb > 1) {
+    __syncthreads();
+    if (L.group != a.rpb - 1) return;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const int v = (i * a.wpr + L.wv) * kWave + L.lane;
+      if (v < a.nvec) {
+        const float* cw = comb + v * VEC;
+        const float* cb = comb + a.N + v * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          accw[i][e] += cw[e];
+          accb[i][e] += cb[e];
+        }
+      }
+    }
+  }
+  const Rsrc rdw = make_rsrc(pw, static_cast<uint32_t>(a.N) * 4u);
+  const Rsrc rdb = make_rsrc(pb, static_cast<uint32_t>(a.N) * 4u);
+  const uint32_t voff32 = L.first_vec() * VEC * 4u;
+  const uint32_t iter32 = static_cast<uint32_t>(a.wpr) * kWave * VEC * 4u;
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    buf_store_f32<VEC, kDefault>(accw[i], rdw, voff32 + i * iter32);
+    buf_store_f32<VEC, kDefault>(accb[i], rdb, voff32 + i * iter32);
   }
 }
 

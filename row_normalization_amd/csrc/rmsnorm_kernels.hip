@@ -277,16 +277,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
 
   // One partial row per workgroup: row groups are added in LDS in group order.
   float* prow = a.partials + static_cast<int64_t>(blockIdx.x) * a.N;
-  if (a.rpb == 1) {
-    const Rsrc rp = make_rsrc(prow, static_cast<uint32_t>(a.N) * 4u);
-    const uint32_t voff32 = static_cast<uint32_t>(L.template wave_vec<ITERS>(0)) * VEC * 4u;
-    const uint32_t iter32 = static_cast<uint32_t>(kWave) * VEC * 4u;
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kDefault>(acc[i], rp, voff32 + i * iter32);
-    return;
-  }
-  for (int g = 0; g < a.rpb; ++g) {
-    __syncthreads();
+  const Rsrc rp = make_rsrc(prow, static_cast<uint32_t>(a.N) * 4u);
+  const uint32_t voff32 = static_cast<uint32_t>(L.template wave_vec<ITERS>(0)) * VEC * 4u;
+  const uint32_t iter32 = static_cast<uint32_t>(kWave) * VEC * 4u;
+  // The last row group adds the sum of the groups before it (left in LDS) to
+  // its own and writes the partial row; every group covers every column, and
+  // lanes past the row's end store out of the descriptor's range.
+  for (int g = 0; g < a.rpb - 1; ++g) {
+    if (g > 0) __syncthreads();
     if (L.group == g) {
 #pragma unroll
       for (int i = 0; i < ITERS; ++i) {
@@ -301,8 +299,20 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
       }
     }
   }
-  __syncthreads();
-  for (int col = threadIdx.x; col < a.N; col += blockDim.x) prow[col] = comb[col];
+  if (a.rpb > 1) {
+    __syncthreads();
+    if (L.group != a.rpb - 1) return;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const int v = L.template wave_vec<ITERS>(i);
+      if (v < a.nvec) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[i][e] += comb[v * VEC + e];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kDefault>(acc[i], rp, voff32 + i * iter32);
 }
 
 // ---------------------------------------------------------------------------
