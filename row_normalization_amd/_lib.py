@@ -111,10 +111,21 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
-def _gpu(*ts: torch.Tensor) -> None:
+def _gpu(*ts: torch.Tensor):
+    """The one GPU every given tensor is on.  Raises for a CPU tensor (there is
+    no CPU path) and for tensors on different GPUs (a kernel launched on one
+    device cannot use another device's pointers)."""
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("the RMSNorm library takes GPU tensors only (no CPU path)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"all tensors of a call must be on one GPU (found {dev} and {t.device})")
+    return dev
 
 
 def _rows(t: torch.Tensor, name: str) -> tuple[int, int, int]:
@@ -153,9 +164,11 @@ def _scratch_bytes(t, name: str, need_elems: int = 0) -> int:
     return t.numel() * t.element_size()
 
 
-def _stream(stream) -> int:
+def _stream(stream, dev) -> int:
+    """The HIP stream to launch on: the given one, else the current stream of
+    the tensors' device."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(dev).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -173,13 +186,14 @@ def rmsnorm_fwd(x, gamma, y, rstd, eps: float = 1e-6, gemma: bool = False, round
 
     ``round_normed`` rounds x * r to the I/O dtype before the weight multiply
     (the Hugging Face order); by default y is rounded once."""
-    _gpu(x, gamma, y, rstd)
+    dev = _gpu(x, gamma, y, rstd)
     M, N, stride = _rows(x, "x")
     _same_layout(x, y, "y", stride)
     _vec(gamma, N, x.dtype, "gamma")
     _vec(rstd, M, torch.float32, "rstd")
-    st = lib().rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, stride, float(eps), _dtype_code(x),
-                           _flags(gemma, round_normed), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, stride, float(eps), _dtype_code(x),
+                               _flags(gemma, round_normed), _stream(stream, dev))
     _check(st, "rmsnorm_fwd")
 
 
@@ -204,34 +218,37 @@ def _bwd_checks(x, gamma, dy, rstd, dx):
 def rmsnorm_bwd_rows(x, gamma, dy, rstd, dx, workspace, gemma: bool = False, stream=None) -> int:
     """dx (may be dy itself) and per-workgroup dgamma partial rows; returns the partial-row count."""
     M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
-    _gpu(workspace)
+    dev = _gpu(x, workspace)
     wbytes = _scratch_bytes(workspace, "workspace")
     rows = _c_i64(0)
-    st = lib().rmsnorm_bwd_rows(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(workspace),
-                                wbytes, M, N, stride, _dtype_code(x),
-                                _flags(gemma), ctypes.byref(rows), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().rmsnorm_bwd_rows(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(workspace),
+                                    wbytes, M, N, stride, _dtype_code(x),
+                                    _flags(gemma), ctypes.byref(rows), _stream(stream, dev))
     _check(st, "rmsnorm_bwd_rows")
     return int(rows.value)
 
 
 def rmsnorm_dgamma_reduce(partials, rows: int, N: int, dgamma, stream=None) -> None:
     """dgamma[j] = sum of the first ``rows`` rows of the [rows, N] fp32 partials."""
-    _gpu(partials, dgamma)
+    dev = _gpu(partials, dgamma)
     _vec(dgamma, N, torch.float32, "dgamma")
     if rows > 0:
         _scratch_bytes(partials, "partials", int(rows) * int(N))
-    st = lib().rmsnorm_dgamma_reduce(_ptr(partials), int(rows), int(N), _ptr(dgamma), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().rmsnorm_dgamma_reduce(_ptr(partials), int(rows), int(N), _ptr(dgamma), _stream(stream, dev))
     _check(st, "rmsnorm_dgamma_reduce")
 
 
 def rmsnorm_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, gemma: bool = False, stream=None) -> None:
     """Full backward: dx (may be dy itself) and dgamma (fp32, overwritten)."""
     M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
-    _gpu(dgamma, workspace)
+    dev = _gpu(x, dgamma, workspace)
     _vec(dgamma, N, torch.float32, "dgamma")
     wbytes = _scratch_bytes(workspace, "workspace")
-    st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
-                           wbytes, M, N, stride, _dtype_code(x), _flags(gemma), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
+                               wbytes, M, N, stride, _dtype_code(x), _flags(gemma), _stream(stream, dev))
     _check(st, "rmsnorm_bwd")
 
 
@@ -246,15 +263,16 @@ def _vec_f32(t, n: int, name: str) -> None:
 
 def layernorm_fwd(x, weight, bias, y, mean, rstd, eps: float = 1e-5, stream=None) -> None:
     """y = (x - mean) * rstd * weight + bias, and the per-row mean and rstd, on the GPU."""
-    _gpu(x, weight, bias, y, mean, rstd)
+    dev = _gpu(x, weight, bias, y, mean, rstd)
     M, N, stride = _rows(x, "x")
     _same_layout(x, y, "y", stride)
     _vec(weight, N, x.dtype, "weight")
     _vec(bias, N, x.dtype, "bias")
     _vec_f32(mean, M, "mean")
     _vec_f32(rstd, M, "rstd")
-    st = lib().layernorm_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), _ptr(mean), _ptr(rstd), M, N, stride,
-                             float(eps), _dtype_code(x), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().layernorm_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(y), _ptr(mean), _ptr(rstd), M, N, stride,
+                                 float(eps), _dtype_code(x), _stream(stream, dev))
     _check(st, "layernorm_fwd")
 
 
@@ -281,36 +299,39 @@ def layernorm_bwd_rows(x, weight, dy, mean, rstd, dx, workspace, stream=None) ->
     """dx (may be dy itself) and per-workgroup dw / db partial rows; returns P, the
     partial-row count (dw partials in rows [0, P), db partials in rows [P, 2P))."""
     M, N, stride = _ln_bwd_checks(x, weight, dy, mean, rstd, dx)
-    _gpu(workspace)
+    dev = _gpu(x, workspace)
     wbytes = _scratch_bytes(workspace, "workspace")
     rows = _c_i64(0)
-    st = lib().layernorm_bwd_rows(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(workspace),
-                                  wbytes, M, N, stride, _dtype_code(x),
-                                  ctypes.byref(rows), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().layernorm_bwd_rows(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx),
+                                      _ptr(workspace), wbytes, M, N, stride, _dtype_code(x),
+                                      ctypes.byref(rows), _stream(stream, dev))
     _check(st, "layernorm_bwd_rows")
     return int(rows.value)
 
 
 def layernorm_dwdb_reduce(partials, rows: int, N: int, dw, db, stream=None) -> None:
     """dw[j] = sum of partials[p, j] over p < rows; db[j] = sum of partials[rows + p, j]."""
-    _gpu(partials, dw, db)
+    dev = _gpu(partials, dw, db)
     _vec_f32(dw, N, "dw")
     _vec_f32(db, N, "db")
     if rows > 0:
         _scratch_bytes(partials, "partials", 2 * int(rows) * int(N))
-    st = lib().layernorm_dwdb_reduce(_ptr(partials), int(rows), int(N), _ptr(dw), _ptr(db), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().layernorm_dwdb_reduce(_ptr(partials), int(rows), int(N), _ptr(dw), _ptr(db), _stream(stream, dev))
     _check(st, "layernorm_dwdb_reduce")
 
 
 def layernorm_bwd(x, weight, dy, mean, rstd, dx, dw, db, workspace, stream=None) -> None:
     """Full LayerNorm backward: dx (may be dy itself), dw and db (fp32, overwritten)."""
     M, N, stride = _ln_bwd_checks(x, weight, dy, mean, rstd, dx)
-    _gpu(dw, db, workspace)
+    dev = _gpu(x, dw, db, workspace)
     _vec_f32(dw, N, "dw")
     _vec_f32(db, N, "db")
     wbytes = _scratch_bytes(workspace, "workspace")
-    st = lib().layernorm_bwd(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dw), _ptr(db),
-                             _ptr(workspace), wbytes, M, N, stride, _dtype_code(x), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().layernorm_bwd(_ptr(x), _ptr(weight), _ptr(dy), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dw),
+                                 _ptr(db), _ptr(workspace), wbytes, M, N, stride, _dtype_code(x), _stream(stream, dev))
     _check(st, "layernorm_bwd")
 
 
@@ -319,7 +340,7 @@ def layernorm_bwd(x, weight, dy, mean, rstd, dx, dw, db, workspace, stream=None)
 # ---------------------------------------------------------------------------
 
 def _rope_args(q, cos, sin, positions, seq_len):
-    _gpu(q, cos, sin, positions)
+    dev = _gpu(q, cos, sin, positions)
     if q.dim() != 3:
         raise ValueError("q must be 3-D [tokens, heads, head_dim]")
     T, H, D = q.shape
@@ -335,22 +356,24 @@ def _rope_args(q, cos, sin, positions, seq_len):
                                   not positions.is_contiguous()):
         raise ValueError("positions must be a contiguous int32 tensor of one entry per token")
     seq = int(seq_len) if seq_len is not None else cos.shape[0]
-    return T, H, D, stride, cos.shape[0], seq
+    return T, H, D, stride, cos.shape[0], seq, dev
 
 
 def rope_fwd(q, cos, sin, positions=None, seq_len=None, stream=None) -> None:
     """Rotates q [tokens, heads, head_dim] in place (pairs are the two head halves)."""
-    T, H, D, stride, rows, seq = _rope_args(q, cos, sin, positions, seq_len)
-    st = lib().rope_fwd(_ptr(q), T, H, D, stride, _ptr(cos), _ptr(sin), rows, _ptr(positions), seq, _dtype_code(q),
-                        _stream(stream))
+    T, H, D, stride, rows, seq, dev = _rope_args(q, cos, sin, positions, seq_len)
+    with torch.cuda.device(dev):
+        st = lib().rope_fwd(_ptr(q), T, H, D, stride, _ptr(cos), _ptr(sin), rows, _ptr(positions), seq,
+                            _dtype_code(q), _stream(stream, dev))
     _check(st, "rope_fwd")
 
 
 def rope_bwd(dq, cos, sin, positions=None, seq_len=None, stream=None) -> None:
     """The inverse rotation (sin negated) of the gradient dq, in place."""
-    T, H, D, stride, rows, seq = _rope_args(dq, cos, sin, positions, seq_len)
-    st = lib().rope_bwd(_ptr(dq), T, H, D, stride, _ptr(cos), _ptr(sin), rows, _ptr(positions), seq,
-                        _dtype_code(dq), _stream(stream))
+    T, H, D, stride, rows, seq, dev = _rope_args(dq, cos, sin, positions, seq_len)
+    with torch.cuda.device(dev):
+        st = lib().rope_bwd(_ptr(dq), T, H, D, stride, _ptr(cos), _ptr(sin), rows, _ptr(positions), seq,
+                            _dtype_code(dq), _stream(stream, dev))
     _check(st, "rope_bwd")
 
 
@@ -363,16 +386,18 @@ def _elementwise_layout(ref, others, names):
 
 def swiglu_fwd(e, g, h, stream=None) -> None:
     """h = T(T(silu(e)) * g) over [M, N] (h may be e or g itself)."""
-    _gpu(e, g, h)
+    dev = _gpu(e, g, h)
     M, N, stride = _elementwise_layout(e, (g, h), ("e", "g", "h"))
-    st = lib().swiglu_fwd(_ptr(e), _ptr(g), _ptr(h), M, N, stride, _dtype_code(e), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().swiglu_fwd(_ptr(e), _ptr(g), _ptr(h), M, N, stride, _dtype_code(e), _stream(stream, dev))
     _check(st, "swiglu_fwd")
 
 
 def swiglu_bwd(dh, e, g, h, df, de, stream=None) -> None:
     """h (recomputed), df = dh * T(f) and de = dh * g * silu'(e); each output may be one of the inputs."""
-    _gpu(dh, e, g, h, df, de)
+    dev = _gpu(dh, e, g, h, df, de)
     M, N, stride = _elementwise_layout(e, (dh, g, h, df, de), ("e", "dh", "g", "h", "df", "de"))
-    st = lib().swiglu_bwd(_ptr(dh), _ptr(e), _ptr(g), _ptr(h), _ptr(df), _ptr(de), M, N, stride, _dtype_code(e),
-                          _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib().swiglu_bwd(_ptr(dh), _ptr(e), _ptr(g), _ptr(h), _ptr(df), _ptr(de), M, N, stride, _dtype_code(e),
+                              _stream(stream, dev))
     _check(st, "swiglu_bwd")
