@@ -2,7 +2,8 @@
 // every row operation, dtype, vector width and N in [1, RMSNORM_N_MAX], at
 // three row counts: a plan always exists, covers every column and row, keeps
 // a lane's row data within the register model, fits a 1024-thread workgroup,
-// and keeps the LDS combine buffer within 64 KB.  It also pins the row shapes
+// keeps the LDS combine buffer within 64 KB, and gives no row a wave that
+// lies wholly past N.  It also pins the row shapes
 // the planner picks for a few widths where the ordering of its rules
 // matters.  Built and run by tests/test_plan.py; prints one summary line and
 // exits non-zero on failure.
@@ -27,7 +28,9 @@ int main() {
             const int64_t lds = p.rpb > 1 ? (op == RowOp::kLnBwd ? 8 : 4) * N : 0;
             const bool ok = p.iters > 0 && p.vec * p.iters <= lane_elems_cap(op, elsize(dt)) && p.threads() <= 1024 &&
                             int64_t(p.iters) * kWave * p.wpr * vec >= N && lds <= 65536 &&
-                            p.grid * p.row_iters * p.rpb >= M && (!bwd || p.grid <= kBwdGridMax);
+                            p.grid * p.row_iters * p.rpb >= M && (!bwd || p.grid <= kBwdGridMax) &&
+                            // no wave of a row lies wholly past N (in either lane mapping)
+                            (p.wpr == 1 || int64_t(p.wpr - 1) * p.iters * kWave < N / vec);
             if (!ok && bad++ < 10)
               std::printf("bad plan: dtype=%d op=%d N=%ld vec=%d M=%ld iters=%d wpr=%d rpb=%d grid=%ld\n", dt,
                           static_cast<int>(op), static_cast<long>(N), vec, static_cast<long>(M), p.iters, p.wpr, p.rpb,
