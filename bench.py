@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--ln-ns", type=int, nargs="*", default=None,
                     help="LayerNorm sweep points (N) to run; default: the chapter's 30 points")
     ap.add_argument("--no-elementwise", action="store_true", help="skip the RoPE and SwiGLU legs")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the plain streaming kernels timed as the reference for the row kernels")
     return ap.parse_args()
 
 
@@ -480,12 +482,40 @@ def cpu_baseline(w: wl.Workload, seconds: float, all_cores_seconds: float) -> di
     return out
 
 
+CEILING_PROBE = os.path.join(ROOT, "tests", "native", "bin", "stream_ceiling")
+
+
+def stream_ceiling():
+    """GB/s of plain streaming kernels (16-byte nontemporal vectors, 256 MiB per
+    operand) for the read/write mixes of the row kernels: read only, one read
+    per write, two reads per write (tests/native/stream_ceiling.hip).  Run as a
+    child process before this process touches the GPU.  None if the probe has
+    not been built."""
+    import subprocess
+
+    if not os.path.exists(CEILING_PROBE):
+        print(f"[ceiling] {CEILING_PROBE} not built; skipped", file=sys.stderr, flush=True)
+        return None
+    r = subprocess.run([CEILING_PROBE], capture_output=True, text=True, timeout=180)
+    if r.returncode != 0:
+        print(f"[ceiling] probe failed ({r.returncode}): {r.stderr.strip()[-300:]}", file=sys.stderr, flush=True)
+        return None
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    print(f"[ceiling] {res}", file=sys.stderr, flush=True)
+    # the JSON line keeps the best shape of each mix; the probe itself lists all
+    for mix in ("read", "read1_write1", "read2_write1"):
+        res[mix].pop("hot_gbps_by_shape", None)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this path is measured on a single MI355X; "
               "multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
+    # before torch initialises the GPU in this process
+    ceiling = None if args.no_ceiling else stream_ceiling()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -550,6 +580,10 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": b["bwd_rows"], "kernel_sha": h},
         "device": device_info(),
+        "stream_ceiling": ceiling,
+        "kernels_vs_ceiling": None if not ceiling else {
+            "fwd": round(b["fwd"] / kern["fwd"]["mean_s"] / 1e9 / ceiling["read1_write1"]["hot_gbps"], 4),
+            "bwd_rows": round(achieved / ceiling["read2_write1"]["hot_gbps"], 4)},
     }
     del path
     torch.cuda.empty_cache()

@@ -83,6 +83,13 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print("+", " ".join(example), flush=True)
     _run(example)
+    # the streaming-ceiling probe bench.py reports beside the kernels
+    # (tests/native/stream_ceiling.hip)
+    probe = [hipcc, *HIP_FLAGS, os.path.join(ROOT, "tests", "native", "stream_ceiling.hip"),
+             "-o", os.path.join(EXAMPLE_DIR, "stream_ceiling")]
+    if verbose:
+        print("+", " ".join(probe), flush=True)
+    _run(probe)
     return LIB
 
 
