@@ -102,8 +102,8 @@ inline int choose_vec(int dtype, int64_t N, int64_t stride, std::initializer_lis
 // Waves per row and vectors per lane.  Candidates: 1..16 waves per row, a
 // compiled register-array length within the lane's register budget, no wave
 // without work.  The smallest key wins, compared in this order:
-//   1. waste (covered minus real vectors) above a quarter of the row;
-//   2. one vector per lane in a row of more than two waves;
+//   1. one vector per lane in a row of more than two waves;
+//   2. waste (covered minus real vectors) above a quarter of the row;
 //   3. 16-bit I/O, forward: a row of more than kFwdRowWaves waves;
 //   4. 16-bit I/O: distance from `target` vectors per lane, then waste;
 //      fp32 I/O: waste, then distance from `target`;
@@ -111,10 +111,14 @@ inline int choose_vec(int dtype, int64_t N, int64_t stride, std::initializer_lis
 // Measured on MI355X (forward and backward, M = 4096 and 16384): one vector
 // per lane in rows of 9-15 waves ran 15-40 % slower than two vectors in
 // half as many waves with a partly empty last wave (e.g. bf16 16384 x 7680
-// forward 129 -> 82 us); 16-bit rows of 10-16 waves in the forward 7-17 %
-// slower than 5-8 waves with 4 vectors; for fp32 rows, where a vector holds
-// half the elements, the least waste was within 2 % of the best shape and the
-// 16-bit order up to 6 % slower.
+// forward 129 -> 82 us), and in rows of 3-7 waves 4-27 % slower than two or
+// four vectors even with more than a quarter of the vectors empty (bf16
+// 16384 x 3200 as 4 x 2 instead of 7 x 1: forward 49.4 -> 37.2 us, backward
+// 57.4 -> 51.5 us; 16384 x 2304 backward as 3 x 2 instead of 5 x 1: 49.1 ->
+// 38.5 us; fp32 N = 704, 1100, 1600 alike); 16-bit rows of 10-16 waves in the
+// forward 7-17 % slower than 5-8 waves with 4 vectors; for fp32 rows, where a
+// vector holds half the elements, the least waste was within 2 % of the best
+// shape and the 16-bit order up to 6 % slower.
 inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool backward, int* wpr, int* iters) {
   bool found = false;
   std::tuple<bool, bool, bool, int64_t, int64_t, int> best{};
@@ -124,7 +128,7 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
       if (w > 1 && int64_t(it) * kWave * (w - 1) >= nvec) continue;
       const int64_t waste = int64_t(it) * kWave * w - nvec;
       const int64_t dist = it > target ? it - target : target - it;
-      const auto key = std::make_tuple(waste * 4 > nvec, it == 1 && w > 2, narrow && !backward && w > kFwdRowWaves,
+      const auto key = std::make_tuple(it == 1 && w > 2, waste * 4 > nvec, narrow && !backward && w > kFwdRowWaves,
                                        narrow ? dist : waste, narrow ? waste : dist, w);
       if (!found || key < best) {
         found = true;
@@ -151,23 +155,22 @@ inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int es, int lane_elems, 
     p.iters = 0;  // cannot happen for N <= RMSNORM_N_MAX
     return p;
   }
-  // 16-bit rows the rule gives three waves (six-wave workgroups): N =
-  // 1232-1536 as 3 x 1, 2464-3072 as 3 x 2.  The forward runs them as one
-  // wave where four or five 16-byte vectors per lane cover the row (no
-  // cross-wave sum, eight rows per workgroup), the backward runs 3 x 1 rows
-  // as 2 x 2 (eight-wave workgroups).  Measured on MI355X: forward 12-25 %
+  // 16-bit forward rows of 129-320 vectors (N = 1032-2560) run as one wave
+  // of four or five 16-byte vectors per lane (no cross-wave sum, eight rows
+  // per workgroup) where the rule gives them three waves or more than a
+  // quarter of the covered vectors empty: N = 1032-1632 (2 x 2 with a
+  // partly empty second wave), 2464-2560 (3 x 2); 2056-2456 get one wave
+  // from the rule itself.  Measured on MI355X against 3 x 1 and 3 x 2: 12-25 %
   // faster at N = 1280 and 1536 (M = 4096 to 65536, both norms), 5-12 % at
-  // N = 2560; backward 4-12 % at N = 1280 and 1536.  Wider rows keep three
-  // waves (forward one wave of 8 vectors or 4 x 2, backward 4 x 2:
-  // -6 ... +20 %, LayerNorm slower).
-  if (es == 2 && vec * es == 16 && p.wpr == 3) {
-    if (!backward && nvec <= 5 * kWave && cap >= 5) {
-      p.wpr = 1;
-      p.iters = nvec <= 4 * kWave ? 4 : 5;
-    } else if (backward && p.iters == 1) {
-      p.wpr = 2;
-      p.iters = 2;
-    }
+  // N = 2560; against 2 x 2: RMSNorm 16384 x 1096 and 16384 x 1600 16-19 %
+  // and 7 % faster, LayerNorm 4096 x 1160 4 % faster and 4096 x 1600 5 %
+  // slower.  Exactly 256 vectors (N = 2048) keep 2 x 2 (one wave of 4 was up
+  // to 12 % slower), and so do rows of 321-384 (one wave of 8 vectors or
+  // 4 x 2 against 3 x 2: -3 ... +20 %).
+  if (es == 2 && vec * es == 16 && !backward && nvec > 2 * kWave && nvec <= 5 * kWave && cap >= 5 &&
+      (p.wpr == 3 || (int64_t(p.wpr) * p.iters * kWave - nvec) * 4 > nvec)) {
+    p.wpr = 1;
+    p.iters = nvec <= 4 * kWave ? 4 : 5;
   }
   p.rpb = std::max(1, kBlockWaves / p.wpr);
   const int64_t groups = ceil_div(M, p.rpb);

@@ -52,7 +52,10 @@ int main() {
       {2, 16384, RowOp::kRmsFwd, 8, 4},  {2, 16384, RowOp::kRmsBwd, 16, 2},  // forward rows of <= 8 waves
       {2, 13312, RowOp::kLnFwd, 7, 4},   {2, 13312, RowOp::kLnBwd, 13, 2},
       {2, 1536, RowOp::kRmsFwd, 1, 4},   {2, 1536, RowOp::kRmsBwd, 2, 2},    // not 3 x 1
-      {2, 1232, RowOp::kLnFwd, 1, 4},
+      {2, 1232, RowOp::kLnFwd, 1, 4},    {2, 2048, RowOp::kRmsFwd, 2, 2},    // one wave; 2 x 2 where exact
+      {2, 3200, RowOp::kRmsFwd, 4, 2},   {2, 3200, RowOp::kLnBwd, 4, 2},     // not 7 x 1
+      {2, 2304, RowOp::kRmsBwd, 3, 2},   {4, 704, RowOp::kRmsFwd, 2, 2},     // not 5 x 1, 3 x 1
+      {4, 1100, RowOp::kLnBwd, 3, 2},    {4, 1600, RowOp::kRmsBwd, 4, 2},    // not 5 x 1, 7 x 1
       {4, 14848, RowOp::kRmsFwd, 12, 5}, {4, 7680, RowOp::kRmsFwd, 6, 5},    // fp32: least waste first
       {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
   };

@@ -48,6 +48,8 @@ SMALL = [
     ("bf16", 4100, 14336),
     # forward rows of three waves' width run as one wave of 4 or 5 vectors
     ("f16", 300, 1232), ("bf16", 129, 2504),
+    # more than a quarter of the vectors empty rather than one vector per lane
+    ("f16", 100, 3200), ("bf16", 77, 2304), ("f32", 100, 1100), ("f32", 65, 704),
 ]
 
 

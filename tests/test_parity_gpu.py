@@ -108,6 +108,13 @@ SMALL = [
     # (the last vectors of the lane partly or wholly past N)
     ("bf16", 700, 1232, False, True),
     ("f16", 300, 2504, True, False),
+    # two or four vectors per lane with more than a quarter of the row's
+    # vectors empty, rather than one vector per lane over 3-7 waves
+    ("bf16", 300, 3200, False, True),   # 4 x 2 both ways
+    ("f16", 200, 2304, True, False),    # backward 3 x 2
+    ("f32", 150, 704, False, False),    # 2 x 2
+    ("f32", 90, 1600, True, True),      # 4 x 2
+    ("bf16", 129, 1096, False, False),  # forward one wave of 4
 ]
 
 
