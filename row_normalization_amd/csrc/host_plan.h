@@ -141,11 +141,14 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
   return found;
 }
 
-inline RowPlan plan_rows(int64_t M, int64_t N, int vec, int es, int lane_elems, bool backward) {
+// The launch plan of row operation `op` over M rows of N elements of `es`
+// bytes, read in vectors of `vec` elements.
+inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
   RowPlan p{};
   p.vec = vec;
+  const bool backward = op == RowOp::kRmsBwd || op == RowOp::kLnBwd;
   const int64_t nvec = N / vec;
-  const int cap = std::min(kItersMax, std::max(1, lane_elems / vec));
+  const int cap = std::min(kItersMax, std::max(1, lane_elems_cap(op, es) / vec));
   // The forward prefers rows of at most kFwdRowWaves waves, with more vectors
   // per lane beyond that (measured at N = 16384 bf16: 8 waves x 4 vectors ran
   // 4 % faster than 16 x 2); the backward keeps kLaneVectors.

@@ -57,7 +57,7 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
                                const float* rstd, void* dx, void* workspace, int64_t M, int64_t N, int64_t stride,
                                int dtype, int64_t* rows_written, hipStream_t stream) {
   const int vec = choose_vec(dtype, N, stride, {x, weight, dy, dx});
-  const RowPlan p = plan_rows(M, N, vec, elsize(dtype), lane_elems_cap(RowOp::kLnBwd, elsize(dtype)), true);
+  const RowPlan p = plan_rows(RowOp::kLnBwd, M, N, vec, elsize(dtype));
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnBwdArgs a{};
   a.x = x;
@@ -115,7 +115,7 @@ int layernorm_fwd(const void* x, const void* weight, const void* bias, void* y, 
   if (overlap(sy, sm) || overlap(sy, sr) || overlap(sm, sr)) return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, weight, bias, y});
-  const RowPlan p = plan_rows(M, N, vec, elsize(dtype), lane_elems_cap(RowOp::kLnFwd, elsize(dtype)), false);
+  const RowPlan p = plan_rows(RowOp::kLnFwd, M, N, vec, elsize(dtype));
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnFwdArgs a{};
   a.x = x;

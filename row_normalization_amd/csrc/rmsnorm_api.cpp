@@ -58,7 +58,7 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
                             void* workspace, int64_t M, int64_t N, int64_t stride, int dtype, int flags,
                             int64_t* rows_written, hipStream_t stream) {
   const int vec = choose_vec(dtype, N, stride, {x, gamma, dy, dx});
-  const RowPlan p = plan_rows(M, N, vec, elsize(dtype), lane_elems_cap(RowOp::kRmsBwd, elsize(dtype)), true);
+  const RowPlan p = plan_rows(RowOp::kRmsBwd, M, N, vec, elsize(dtype));
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   BwdArgs a{};
   a.x = x;
@@ -110,7 +110,7 @@ int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t 
     return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, gamma, y});
-  const RowPlan p = plan_rows(M, N, vec, elsize(dtype), lane_elems_cap(RowOp::kRmsFwd, elsize(dtype)), false);
+  const RowPlan p = plan_rows(RowOp::kRmsFwd, M, N, vec, elsize(dtype));
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   FwdArgs a{};
   a.x = x;

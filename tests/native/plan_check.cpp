@@ -23,7 +23,7 @@ int main() {
           if (N % vec) continue;
           const bool bwd = op == RowOp::kRmsBwd || op == RowOp::kLnBwd;
           for (int64_t M : {int64_t(1), int64_t(4096), int64_t(1) << 20}) {
-            const RowPlan p = plan_rows(M, N, vec, elsize(dt), lane_elems_cap(op, elsize(dt)), bwd);
+            const RowPlan p = plan_rows(op, M, N, vec, elsize(dt));
             ++n;
             const int64_t lds = p.rpb > 1 ? (op == RowOp::kLnBwd ? 8 : 4) * N : 0;
             const bool ok = p.iters > 0 && p.vec * p.iters <= lane_elems_cap(op, elsize(dt)) && p.threads() <= 1024 &&
@@ -60,8 +60,7 @@ int main() {
       {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
   };
   for (const Pin& q : pins) {
-    const bool bwd = q.op == RowOp::kRmsBwd || q.op == RowOp::kLnBwd;
-    const RowPlan p = plan_rows(4096, q.N, 16 / q.es, q.es, lane_elems_cap(q.op, q.es), bwd);
+    const RowPlan p = plan_rows(q.op, 4096, q.N, 16 / q.es, q.es);
     ++n;
     if (p.wpr != q.wpr || p.iters != q.iters) {
       ++bad;
