@@ -83,6 +83,14 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print("+", " ".join(example), flush=True)
     _run(example)
+    # the planner's exhaustive check; with --widths it lists the widths at
+    # which the GPU tests run every row shape the planner can emit
+    plan_check = ["g++", "-std=c++17", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+                  f"-I{os.path.join(ROCM, 'include')}", f"-I{CSRC}",
+                  os.path.join(ROOT, "tests", "native", "plan_check.cpp"), "-o", os.path.join(EXAMPLE_DIR, "plan_check")]
+    if verbose:
+        print("+", " ".join(plan_check), flush=True)
+    _run(plan_check)
     # the streaming-ceiling probe bench.py reports beside the kernels
     # (tests/native/stream_ceiling.hip)
     probe = [hipcc, *HIP_FLAGS, os.path.join(ROOT, "tests", "native", "stream_ceiling.hip"),

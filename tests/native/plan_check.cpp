@@ -11,9 +11,47 @@
 
 #include "host_plan.h"
 
+#include <cstring>
+#include <map>
+#include <set>
+#include <tuple>
+
 using namespace rmsn;
 
-int main() {
+// With --widths: for every distinct plan (operation, element size, vector
+// width, waves per row, vectors per lane) over N <= RMSNORM_N_MAX, the
+// smallest and the largest N that get it, as lines "rms|ln <element size> N"
+// (each norm's forward and backward both run at every width listed for it).
+// The GPU test tests/test_plan_coverage_gpu.py runs each line against the
+// oracle, so every row shape the planner can emit runs at least once.
+static int print_widths() {
+  std::map<std::tuple<int, int, int, int, int>, std::pair<int64_t, int64_t>> first_last;
+  const RowOp ops[4] = {RowOp::kRmsFwd, RowOp::kRmsBwd, RowOp::kLnFwd, RowOp::kLnBwd};
+  for (int es : {2, 4})
+    for (RowOp op : ops)
+      for (int vec = 16 / es; vec >= 1; vec /= 2)
+        for (int64_t N = vec; N <= RMSNORM_N_MAX; N += vec) {
+          if (vec < 16 / es && N % (2 * vec) == 0) continue;  // N alone would allow a wider vector
+          const RowPlan p = plan_rows(op, 33, N, vec, es);
+          const auto key = std::make_tuple(static_cast<int>(op), es, vec, p.wpr, p.iters);
+          auto it = first_last.find(key);
+          if (it == first_last.end())
+            first_last[key] = {N, N};
+          else
+            it->second.second = N;
+        }
+  std::set<std::tuple<int, int, int64_t>> widths;  // (LayerNorm?, element size, N)
+  for (const auto& [key, range] : first_last) {
+    const int ln = std::get<0>(key) >= static_cast<int>(RowOp::kLnFwd);
+    widths.insert({ln, std::get<1>(key), range.first});
+    widths.insert({ln, std::get<1>(key), range.second});
+  }
+  for (const auto& [ln, es, N] : widths) std::printf("%s %d %ld\n", ln ? "ln" : "rms", es, static_cast<long>(N));
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && std::strcmp(argv[1], "--widths") == 0) return print_widths();
   long bad = 0, n = 0;
   const RowOp ops[4] = {RowOp::kRmsFwd, RowOp::kRmsBwd, RowOp::kLnFwd, RowOp::kLnBwd};
   for (int dt = 0; dt < 3; ++dt)
