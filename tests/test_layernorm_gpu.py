@@ -104,6 +104,19 @@ def test_inputs_untouched():
     assert torch.equal(run.x_gpu.cpu(), run.inputs["x"])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [2, 3, 64, 1000])
+def test_near_constant_rows(N, dtype):
+    """Rows whose spread is near or below sqrt(eps) next to their values
+    (x = 5 + 1e-3 z): the variance is about eps / 10, so eps decides rstd, and
+    in fp32 the centering x - mean is what limits y and dx (the centering
+    allowance of tests.parity_ln)."""
+    w = wl.Workload(f"ln_near_const_{dtype}_{N}", dtype, 300, N, x=("normal", 5.0, 1e-3), gamma=wl.LN1.gamma,
+                    beta=wl.LN1.beta, dy=wl.LN1.dy, eps=1e-5, seed=N)
+    _print_case(w.name)
+    compare_ln_with_oracle(LnRun(w))
+
+
 def test_zero_rows_gives_zero_gradients():
     w = wl.LN1.scaled(M=0, N=256)
     _print_case(w.name)
