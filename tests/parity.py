@@ -26,10 +26,13 @@ dx is the difference of two terms, r*u and x*r^3*m.  Where they cancel (a
 row of one column, N = 1, is the extreme: dx = r*u*eps/(x^2 + eps)), fp32
 evaluation of the difference leaves an absolute error of a few units in the
 last place of r*u no matter how the kernel is written.  dx's bounds therefore
-get an allowance proportional to the oracle's direct term |r*u|: 2^-22 |r u|
-per element for fp32 (about two fp32 ulps) and 2^-20 ||r u|| in the bf16
+get an allowance proportional to the oracle's direct term |r*u|: 2^-20 |r u|
+per element for fp32 (eight fp32 ulps: the roundings of r*u, of r^3 * m and of
+the fused difference make about three, and rsqrt's error of up to one ulp in
+r reaches dx = r*u*(1 - x^2 r^2) twice over, since d dx / d r ~ -2u there; at
+N = 1 an rsqrt one ulp low gives 2.2 ulps) and 2^-18 ||r u|| in the bf16
 norm-wise bound.  Away from cancellation |r u| ~ |dx| and the allowance is
-below 1e-6 of the bound; a dropped r^3 term still misses by ~1e-2.
+below 1e-5 of the bound; a dropped r^3 term still misses by ~1e-2.
 """
 from __future__ import annotations
 
@@ -148,7 +151,8 @@ def compare_with_oracle(run: Run, rows: np.ndarray | None = None) -> dict:
     diag = {}
     diag["y"] = check_close(f"{w.name} y", y[sel], y_o[sel], w.dtype, "y")
     check_rstd(f"{w.name} rstd", r[sel], r_o[sel])
-    direct = r_o[:, None] * dy * oracle.weight(gamma, w.gemma)[None, :]
+    # check_close allows 2^-22 * direct: four times |r u| makes 2^-20 |r u|
+    direct = 4.0 * r_o[:, None] * dy * oracle.weight(gamma, w.gemma)[None, :]
     diag["dx"] = check_close(f"{w.name} dx", dx[sel], dx_o[sel], w.dtype, "dx", direct=direct[sel])
     if w.dtype != "f32" and w.N >= 64:
         diag["dx_invariant"] = check_dx_invariant(f"{w.name} dx", dx[sel], x[sel])
