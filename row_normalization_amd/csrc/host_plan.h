@@ -39,6 +39,7 @@ constexpr int64_t kBwdGridMax = 1024;
 constexpr int64_t kFwdGridMax = 1 << 20;
 constexpr int64_t kFwdPersistentMinSteps = 8;
 constexpr int64_t kFwdPersistentMinWaves = 14;
+constexpr int64_t kLnFwdPersistentMinWaves = 12;
 
 inline int elsize(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
 
@@ -187,17 +188,20 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
   // and 8192 x 16384, 7-9 % for LayerNorm at 4096 x 8192 and larger; 7-wave
   // rows of four vectors (N = 12800-14336 16-bit, fp32 N = 7168) 0.5-3.6 %
   // faster for RMSNorm and 5-10 % for LayerNorm, which loads two weight
-  // vectors per workgroup.  Elsewhere one workgroup per row group is faster:
-  // with fewer waves per CU or two vectors per lane a persistent grid keeps
-  // too few loads in flight (5-wave rows at N = 5120, 10 waves per CU: 8-12 %
-  // slower; 7-wave rows of two vectors at N = 7168: 1-6 % slower; 6-wave rows
-  // of four: -3 ... +3 %), and with 2-4 row groups per workgroup
-  // (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a workgroup queue
-  // behind each other (3-15 % slower).
+  // vectors per workgroup; for LayerNorm also 6-wave rows of four vectors
+  // (12 waves per CU, kLnFwdPersistentMinWaves): 0.7-8 % faster at M = 4096
+  // to 16384, N = 10752-12288 and fp32 N = 6144, where RMSNorm's were -3 ...
+  // +3 %.  Elsewhere one workgroup per row group is faster: with fewer waves
+  // per CU or two vectors per lane a persistent grid keeps too few loads in
+  // flight (5-wave rows at N = 5120, 10 waves per CU: 8-12 % slower; 7-wave
+  // rows of two vectors at N = 7168: 1-6 % slower), and with 2-4 row groups
+  // per workgroup (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a
+  // workgroup queue behind each other (3-15 % slower).
   const int64_t cu_waves = per_cu * p.wpr * p.rpb;
   const bool four_full_vectors = p.iters == 4 && p.vec * es == 16;
   const bool fwd_persistent =
-      (cu_waves == kBwdResidentWaves || (cu_waves >= kFwdPersistentMinWaves && four_full_vectors)) &&
+      (cu_waves == kBwdResidentWaves ||
+       (cu_waves >= (op == RowOp::kLnFwd ? kLnFwdPersistentMinWaves : kFwdPersistentMinWaves) && four_full_vectors)) &&
       groups >= kFwdPersistentMinSteps * kComputeUnits * per_cu;
   const int64_t grid_cap = backward         ? std::min(kBwdGridMax, kComputeUnits * per_cu)
                            : fwd_persistent ? kComputeUnits * per_cu

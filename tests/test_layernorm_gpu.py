@@ -45,7 +45,7 @@ SMALL = [
     # one workgroup per CU, next row's loads in flight (3, 5, 3, 4 rows per workgroup)
     ("f16", 600, 12288), ("bf16", 1100, 9216), ("f32", 513, 8192), ("f16", 1024, 10240),
     # persistent forward with 7-wave rows of four vectors, ragged last row step
-    ("bf16", 4100, 14336),
+    ("bf16", 4100, 14336), ("f16", 4100, 11264), ("f32", 4100, 6144),   # and 6-wave rows (12 waves per CU)
     # forward rows of three waves' width run as one wave of 4 or 5 vectors
     ("f16", 300, 1232), ("bf16", 129, 2504),
     # more than a quarter of the vectors empty rather than one vector per lane
