@@ -91,3 +91,36 @@ def test_found_case(case):
         w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
                         dy=wl.LN1.dy, eps=1e-5, seed=seed)
         compare_ln_with_oracle(LnRun(w, row_stride=N + pad, offset=offset, split_bwd=split, in_place=in_place))
+
+
+def _large_cases(seed: int, n: int):
+    """M in [4096, 20000] (persistent forward grids and many rows per backward
+    workgroup), N in [1, 16384], M * N <= 2.5e7, dense rows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < n:
+        M, N = int(rng.integers(4096, 20001)), int(rng.integers(1, 16385))
+        if M * N > 2.5e7:
+            continue
+        dtype = str(rng.choice(["f32", "bf16", "f16"]))
+        gemma, in_place, split = (bool(v) for v in rng.integers(0, 2, size=3))
+        out.append(("rms" if len(out) % 2 == 0 else "ln", dtype, M, N, gemma, in_place, split))
+    return out
+
+
+LARGE = _large_cases(555, 8)
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[f"{c[0]}-{c[1]}-{c[2]}x{c[3]}" for c in LARGE])
+def test_large_random_case(case):
+    norm, dtype, M, N, gemma, in_place, split = case
+    print("case:", case, flush=True)
+    if norm == "rms":
+        w = (wl.C3 if gemma else wl.C2).scaled(M=M, N=N, dtype=dtype, gemma=gemma, dx_in_place=in_place, seed=M + N)
+        if dtype == "f32":
+            w = w.scaled(dy=("normal", 0.0, 1.0))
+        compare_with_oracle(Run(w, split_bwd=split))
+    else:
+        w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
+                        dy=wl.LN1.dy, eps=1e-5, seed=M + N)
+        compare_ln_with_oracle(LnRun(w, split_bwd=split, in_place=in_place))
