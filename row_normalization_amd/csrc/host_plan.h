@@ -176,6 +176,14 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
     p.wpr = 1;
     p.iters = nvec <= 4 * kWave ? 4 : 5;
   }
+  // A backward row the rule gives one wave of five vectors (fp32 RMSNorm,
+  // N = 1028-1280) runs as 3 x 2: fewer row groups per workgroup to add up at
+  // its end.  Measured on MI355X: 8.6-14 % faster over that range at M = 4096
+  // to 16384.
+  if (backward && p.wpr == 1 && p.iters > 4) {
+    p.wpr = static_cast<int>(ceil_div(nvec, 2 * kWave));
+    p.iters = 2;
+  }
   p.rpb = std::max(1, kBlockWaves / p.wpr);
   const int64_t groups = ceil_div(M, p.rpb);
   int64_t per_cu = 1;
