@@ -176,6 +176,17 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
     p.wpr = 1;
     p.iters = nvec <= 4 * kWave ? 4 : 5;
   }
+  // A 16-bit LayerNorm forward row of 1025-1279 vectors (N = 8200-10232),
+  // which the rule gives 5 waves x 4 vectors, runs as 4 x 5: fewer waves in
+  // its two cross-wave sums, and eight-wave workgroups of two rows.  Measured
+  // on MI355X: 1.4-9.8 % faster at M = 4096 to 16384 (N = 8704, 9056, 9216);
+  // at exactly 1280 vectors (N = 10240, no lane idle in 5 x 4) mixed, -2.8
+  // ... +1.6 %, so 5 x 4 stays.
+  if (op == RowOp::kLnFwd && es == 2 && vec == 8 && p.wpr == 5 && p.iters == 4 && nvec < 4 * 5 * kWave &&
+      cap >= 5) {
+    p.wpr = 4;
+    p.iters = 5;
+  }
   // A backward row the rule gives one wave of five vectors (fp32 RMSNorm,
   // N = 1028-1280) runs as 3 x 2: fewer row groups per workgroup to add up at
   // its end.  Measured on MI355X: 8.6-14 % faster over that range at M = 4096

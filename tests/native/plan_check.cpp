@@ -95,6 +95,8 @@ int main(int argc, char** argv) {
       {2, 2304, RowOp::kRmsBwd, 3, 2},   {4, 704, RowOp::kRmsFwd, 2, 2},     // not 5 x 1, 3 x 1
       {4, 1100, RowOp::kLnBwd, 3, 2},    {4, 1600, RowOp::kRmsBwd, 4, 2},    // not 5 x 1, 7 x 1
       {4, 1200, RowOp::kRmsBwd, 3, 2},                                        // not 1 x 5
+      {2, 9216, RowOp::kLnFwd, 4, 5},    {2, 10240, RowOp::kLnFwd, 5, 4},    // LayerNorm forward
+      {2, 9216, RowOp::kRmsFwd, 5, 4},
       {4, 14848, RowOp::kRmsFwd, 12, 5}, {4, 7680, RowOp::kRmsFwd, 6, 5},    // fp32: least waste first
       {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
   };
