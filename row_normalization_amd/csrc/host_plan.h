@@ -187,6 +187,15 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
     p.wpr = 4;
     p.iters = 5;
   }
+  // Likewise 16-bit LayerNorm forward rows the rule gives 6 or 7 waves of two
+  // vectors (N = 5128-7168) run as 3 x 4 or 4 x 4: half the waves, and a
+  // persistent grid from M = 8192 on.  Measured on MI355X (N = 5264, 5896,
+  // 6144, 6432, 7000, 7168): 3.3-10.5 % faster at M = 8192 and 16384,
+  // -0.8 ... +1.3 % at M = 4096.
+  if (op == RowOp::kLnFwd && es == 2 && vec == 8 && p.iters == 2 && (p.wpr == 6 || p.wpr == 7)) {
+    p.wpr = p.wpr == 6 ? 3 : 4;
+    p.iters = 4;
+  }
   // A backward row the rule gives one wave of five vectors (fp32 RMSNorm,
   // N = 1028-1280) runs as 3 x 2: fewer row groups per workgroup to add up at
   // its end.  Measured on MI355X: 8.6-14 % faster over that range at M = 4096

@@ -96,7 +96,8 @@ int main(int argc, char** argv) {
       {4, 1100, RowOp::kLnBwd, 3, 2},    {4, 1600, RowOp::kRmsBwd, 4, 2},    // not 5 x 1, 7 x 1
       {4, 1200, RowOp::kRmsBwd, 3, 2},                                        // not 1 x 5
       {2, 9216, RowOp::kLnFwd, 4, 5},    {2, 10240, RowOp::kLnFwd, 5, 4},    // LayerNorm forward
-      {2, 9216, RowOp::kRmsFwd, 5, 4},
+      {2, 9216, RowOp::kRmsFwd, 5, 4},   {2, 5264, RowOp::kLnFwd, 3, 4},
+      {2, 6432, RowOp::kLnFwd, 4, 4},    {2, 6432, RowOp::kRmsFwd, 7, 2},
       {4, 14848, RowOp::kRmsFwd, 12, 5}, {4, 7680, RowOp::kRmsFwd, 6, 5},    // fp32: least waste first
       {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
   };
