@@ -2,24 +2,28 @@
 
 One step = the whole path over one batch: forward (y, r), backward row pass
 (dx written in place over dy, per-workgroup dgamma partials) and the dgamma
-column reduction — three launches through the C ABI on torch's current HIP
-stream.  Inputs are seeded synthetic tensors already resident in HBM.  The
-default workload is bf16 M=16384 N=8192 with the Gemma (1+gamma) weight and an
-in-place dx: the configuration the metric is quoted on.
+column reduction -- three launches through the C ABI.  Inputs are seeded
+synthetic tensors already resident in HBM.  The default workload is bf16
+M=16384 N=8192 with the Gemma (1+gamma) weight and an in-place dx: the
+configuration the metric is quoted on.
 
 Prints ONE JSON line.  ``value`` is algorithmic bytes of fwd+bwd per step
-divided by the measured step time; ``roofline`` describes the dominant kernel
-(the backward row pass) timed per launch with HIP events on the same stream;
+divided by the step time measured over exactly ``--steps`` timed steps
+(after ``--warmup`` steps and a settle period), all three launches on
+torch's current stream (``schedule``; the step with the column reduction on a
+second stream, overlapping the next forward, is timed beside it).  ``roofline`` describes the dominant kernel
+(the backward row pass) timed per launch with HIP events on its stream.
+``configs`` holds the five RMSNorm workloads measured with the RMSNorm
+tutorial's protocol (median of samples, each an event pair around 20
+back-to-back calls): forward, backward (row pass + reduction) and the step,
+hot (the same buffers every call) and flushed (operand sets rotated so that
+no call finds its operands in the 256 MB Infinity Cache).
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
 workload on this host, on one core (``value``) and sharded over up to 16
-cores (``all_cores``).  ``layernorm`` holds the LayerNorm sweep of the
-LayerNorm chapter's benchmark (M = 4096, fp16, N = 1024 .. 15872): per point,
-the forward and the backward (row pass + dw/db reduction) timed per launch
-with events, as GB/s by the chapter's formulas (2 and 3 * numel * elsize per
-launch) and as a fraction of the HBM peak on algorithmic bytes.  ``rope``
-and ``swiglu`` time the two elementwise ops of the Unsloth walkthrough on
-their workloads (RoPE: 8192 tokens x 32 heads x 128, bf16, in place; SwiGLU:
-11136 x 14336 bf16), forward and backward, per launch with events.
+cores (``all_cores``).  ``layernorm`` holds the LayerNorm chapter's sweep
+(M = 4096, fp16, N = 1024 .. 15872), ``rope`` and ``swiglu`` the two
+elementwise ops of the Unsloth walkthrough on their workloads, each timed
+with the same protocol.
 """
 from __future__ import annotations
 
@@ -62,8 +66,16 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--cpu-all-cores-seconds", type=float, default=8.0,
                     help="wall time of the oracle sample sharded over the host's cores (0: skip)")
+    ap.add_argument("--schedule", default="one_stream", choices=("one_stream", "overlapped_reduce"),
+                    help="the timed step's schedule: all three launches on one stream, or the dgamma reduction on "
+                         "a second stream overlapping the next forward (the other is timed for context; measured "
+                         "on MI355X the overlapped one was 3 %% slower: its two cross-stream waits per step cost "
+                         "more than the 3.6 us reduction)")
+    ap.add_argument("--samples", type=int, default=SAMPLES,
+                    help=f"samples of {CALLS} back-to-back calls per per-launch or per-config figure (median)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the five-workload protocol block")
     ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
-    ap.add_argument("--ln-steps", type=int, default=50, help="timed launches per LayerNorm sweep point")
+    ap.add_argument("--ln-samples", type=int, default=20, help="samples per LayerNorm sweep point and kernel")
     ap.add_argument("--ln-ns", type=int, nargs="*", default=None,
                     help="LayerNorm sweep points (N) to run; default: the chapter's 30 points")
     ap.add_argument("--no-elementwise", action="store_true", help="skip the RoPE and SwiGLU legs")
@@ -100,51 +112,131 @@ def traffic_from_profile(h: str):
 
 
 class Path:
-    """Device buffers and pre-marshalled C-ABI calls for one workload."""
+    """Device buffers and pre-marshalled C-ABI calls for one workload.
 
-    def __init__(self, w: wl.Workload):
+    ``sets`` operand sets (x, dy, y, rstd, dx, workspace) share one gamma;
+    call ``k`` uses set ``k % sets``, so rotating through enough sets keeps
+    every call's operands out of the caches.  Set 0 holds the generated
+    inputs, the others device copies of them.  Every call's arguments are
+    built once (a launch then costs one ctypes call on the host)."""
+
+    def __init__(self, w: wl.Workload, sets: int = 1):
         import row_normalization_amd as rn
 
         self.w = w
         self.L = rn.lib()
         t = wl.make_inputs(w)
         dev = "cuda"
-        self.x = t["x"].to(dev)
         self.gamma = t["gamma"].to(dev)
-        self.dy = t["dy"].to(dev)
-        self.y = torch.empty_like(self.x)
-        self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
-        self.dx = self.dy if w.dx_in_place else torch.empty_like(self.dy)
+        x0, dy0 = t["x"].to(dev), t["dy"].to(dev)
+        del t
+        self.sets = sets
+        self.x = [x0] + [x0.clone() for _ in range(sets - 1)]
+        self.dy = [dy0] + [dy0.clone() for _ in range(sets - 1)]
+        self.dy_pristine = dy0.clone() if w.dx_in_place else None
+        self.y = [torch.empty_like(x0) for _ in range(sets)]
+        self.rstd = [torch.empty(w.M, dtype=torch.float32, device=dev) for _ in range(sets)]
+        self.dx = self.dy if w.dx_in_place else [torch.empty_like(dy0) for _ in range(sets)]
         self.dgamma = torch.empty(w.N, dtype=torch.float32, device=dev)
         self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(w.M, w.N, w.torch_dtype)
-        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device=dev)
+        # two workspaces per set: the overlapped schedule alternates between them
+        self.ws = [torch.empty(max(self.ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+                   for _ in range(2 * sets)]
         self.dtype = DTYPE_CODE[w.dtype]
-        self.stream = torch.cuda.current_stream().cuda_stream
         self.rows = ctypes_int64()
-        self.partial_rows = None
-
-    def fwd(self):
-        st = self.L.rmsnorm_fwd(self.x.data_ptr(), self.gamma.data_ptr(), self.y.data_ptr(), self.rstd.data_ptr(),
-                                self.w.M, self.w.N, self.w.N, self.w.eps, self.dtype, int(self.w.gemma), self.stream)
-        assert st == 0, st
-
-    def bwd_rows(self):
-        st = self.L.rmsnorm_bwd_rows(self.x.data_ptr(), self.gamma.data_ptr(), self.dy.data_ptr(),
-                                     self.rstd.data_ptr(), self.dx.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
-                                     self.w.M, self.w.N, self.w.N, self.dtype, int(self.w.gemma), self.rows.ref,
-                                     self.stream)
-        assert st == 0, st
-        self.partial_rows = self.rows.value
-
-    def reduce(self):
-        st = self.L.rmsnorm_dgamma_reduce(self.ws.data_ptr(), self.partial_rows, self.w.N, self.dgamma.data_ptr(),
-                                          self.stream)
-        assert st == 0, st
-
-    def step(self):
-        self.fwd()
+        self.stream = torch.cuda.current_stream().cuda_stream
+        M, N, flags = w.M, w.N, int(w.gemma)
+        self._fwd = [(self.x[k].data_ptr(), self.gamma.data_ptr(), self.y[k].data_ptr(), self.rstd[k].data_ptr(), M,
+                      N, N, w.eps, self.dtype, flags) for k in range(sets)]
+        self._rows = [[(self.x[k].data_ptr(), self.gamma.data_ptr(), self.dy[k].data_ptr(), self.rstd[k].data_ptr(),
+                        self.dx[k].data_ptr(), self.ws[2 * k + b].data_ptr(), self.ws_bytes, M, N, N, self.dtype,
+                        flags, self.rows.ref) for b in range(2)] for k in range(sets)]
         self.bwd_rows()
-        self.reduce()
+        torch.cuda.synchronize()
+        self.partial_rows = self.rows.value
+        self._red = [[(self.ws[2 * k + b].data_ptr(), self.partial_rows, N, self.dgamma.data_ptr())
+                      for b in range(2)] for k in range(sets)]
+
+    def fwd(self, k: int = 0, stream=None):
+        st = self.L.rmsnorm_fwd(*self._fwd[k % self.sets], stream or self.stream)
+        assert st == 0, st
+
+    def bwd_rows(self, k: int = 0, ws: int = 0, stream=None):
+        st = self.L.rmsnorm_bwd_rows(*self._rows[k % self.sets][ws], stream or self.stream)
+        assert st == 0, st
+
+    def reduce(self, k: int = 0, ws: int = 0, stream=None):
+        st = self.L.rmsnorm_dgamma_reduce(*self._red[k % self.sets][ws], stream or self.stream)
+        assert st == 0, st
+
+    def bwd(self, k: int = 0):
+        self.bwd_rows(k)
+        self.reduce(k)
+
+    def step(self, k: int = 0):
+        self.fwd(k)
+        self.bwd_rows(k)
+        self.reduce(k)
+
+    def restore(self):
+        """dy back to its generated values in every set (in place, dx overwrote
+        it), then a read sweep so that the copies' dirty cache lines are
+        written back before the timed calls."""
+        if self.dy_pristine is not None:
+            for d in self.dy:
+                d.copy_(self.dy_pristine)
+            flush_by_reading()
+
+
+_FLUSH = None
+
+
+def flush_by_reading() -> None:
+    """Read a 1 GiB buffer: it takes the place of everything in L2 and the
+    256 MB Infinity Cache, and any dirty line there is written back now."""
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    _FLUSH.sum()
+
+
+class OverlappedSteps:
+    """The step with the dgamma column reduction on a second stream: step k's
+    reduction waits for its row pass (an event) and overlaps step k + 1's
+    forward.  The row passes alternate between two workspaces; before the row
+    pass of step k + 2 reuses a workspace, its stream waits for step k's
+    reduction.  Nothing in a training step reads dgamma before the optimizer,
+    so the reduction has only to be done by then.  Both streams have the
+    default priority."""
+
+    def __init__(self, path: Path):
+        self.p = path
+        self.side = torch.cuda.Stream()
+        self.side_handle = self.side.cuda_stream
+        self.rows_done = [torch.cuda.Event() for _ in range(2)]
+        self.reduce_done = [torch.cuda.Event() for _ in range(2)]
+        self.used = [False, False]
+        self.k = 0
+
+    def step(self, _=None):
+        p, b = self.p, self.k % 2
+        main = torch.cuda.current_stream()
+        p.fwd()
+        if self.used[b]:
+            main.wait_event(self.reduce_done[b])  # step k - 2's reduction has read this workspace
+        p.bwd_rows(0, b)
+        self.rows_done[b].record(main)
+        self.side.wait_event(self.rows_done[b])
+        p.reduce(0, b, self.side_handle)
+        self.reduce_done[b].record(self.side)
+        self.used[b] = True
+        self.k += 1
+
+    def join(self):
+        """Make the current stream wait for every reduction issued so far."""
+        for b in range(2):
+            if self.used[b]:
+                torch.cuda.current_stream().wait_event(self.reduce_done[b])
 
 
 class ctypes_int64:
@@ -201,77 +293,117 @@ class LnPath:
                                           self.db.data_ptr(), self.stream)
         assert st == 0, st
 
+    def bwd(self):
+        self.bwd_rows()
+        self.reduce()
+
     def step(self):
         self.fwd()
         self.bwd_rows()
         self.reduce()
 
 
-def layernorm_sweep(steps: int, ns=None) -> dict:
+# The RMSNorm tutorial's protocol ("Benchmark đo thời gian nào?"): warm up,
+# then the median over samples, each an event pair around back-to-back calls.
+SAMPLES = 50
+CALLS = 20
+
+
+def layernorm_sweep(samples: int, ns=None) -> dict:
     """The LayerNorm chapter's sweep: M = 4096 fp16, N = 512 * i, i = 2 .. 31."""
     points = []
     for N in (ns or wl.LN_SWEEP_NS):
         w = wl.ln_sweep(N)
         path = LnPath(w)
-        for _ in range(3):
-            path.step()
-        k = time_kernels(path, steps)
-        t_f, t_r, t_d = (k[n]["mean_s"] for n in ("fwd", "bwd_rows", "dgamma_reduce"))
+        path.step()
+        t_f, t_r, t_d = (time_calls(fn, samples)["median_s"] for fn in (path.fwd, path.bwd_rows, path.reduce))
+        t_b = time_calls(path.bwd, samples)["median_s"]
         b = wl.ln_algorithmic_bytes(w.M, w.N, w.elsize)
         numel_bytes = w.M * w.N * w.elsize
         points.append({
             "N": N,
             "fwd_us": round(t_f * 1e6, 2), "bwd_rows_us": round(t_r * 1e6, 2), "reduce_us": round(t_d * 1e6, 2),
+            "bwd_us": round(t_b * 1e6, 2),
             "fwd_gbps_page_formula": round(2 * numel_bytes / t_f / 1e9, 1),
-            "bwd_gbps_page_formula": round(3 * numel_bytes / (t_r + t_d) / 1e9, 1),
+            "bwd_gbps_page_formula": round(3 * numel_bytes / t_b / 1e9, 1),
             "fwd_frac": round(b["fwd"] / t_f / 1e9 / PEAK_HBM_GBPS, 4),
             "bwd_rows_frac": round(b["bwd_rows"] / t_r / 1e9 / PEAK_HBM_GBPS, 4),
-            "bwd_frac": round(b["bwd"] / (t_r + t_d) / 1e9 / PEAK_HBM_GBPS, 4),
+            "bwd_frac": round(b["bwd"] / t_b / 1e9 / PEAK_HBM_GBPS, 4),
             "partial_rows": path.partial_rows,
         })
-        print(f"[layernorm sweep] N={N}: fwd {points[-1]['fwd_us']} us, bwd {t_r * 1e6 + t_d * 1e6:.1f} us",
+        print(f"[layernorm sweep] N={N}: fwd {points[-1]['fwd_us']} us, bwd {points[-1]['bwd_us']} us",
               file=sys.stderr, flush=True)
         del path
         torch.cuda.empty_cache()
     med = lambda key: float(np.median([p[key] for p in points]))
-    return {"workload": f"layernorm fp16 M={wl.LN_SWEEP_M}, N = 512*i for i = 2..31", "steps_per_point": steps,
+    return {"workload": f"layernorm fp16 M={wl.LN_SWEEP_M}, N = 512*i for i = 2..31",
+            "protocol": f"median of {samples} samples x {CALLS} back-to-back calls",
             "median_fwd_frac": round(med("fwd_frac"), 4), "median_bwd_frac": round(med("bwd_frac"), 4),
             "median_bwd_gbps_page_formula": round(med("bwd_gbps_page_formula"), 1), "points": points}
 
 
-# Untimed work before each per-launch measurement.  On MI355X a new stream of
-# launches runs up to ~15 % slower for its first ~10 ms and then settles (seen
-# in rocprofv3 traces of 150 back-to-back SwiGLU forwards: ~150 us, rising to
-# ~176 us around 6-9 ms in, back to ~152 us from ~15 ms on), so each
-# measurement starts after at least this much work.
+# Untimed work before each measurement.  On MI355X a new stream of launches
+# runs up to ~15 % slower for its first ~10 ms and then settles (seen in
+# rocprofv3 traces of 150 back-to-back SwiGLU forwards: ~150 us, rising to
+# ~176 us around 6-9 ms in, back to ~152 us from ~15 ms on).
 WARM_SECONDS = 0.025
+# Before the headline's timed steps, whatever --warmup asks for: its 20-200
+# timed steps last only 4-45 ms.
+SETTLE_SECONDS = 0.1
 
 
-def warm_up(fn, seconds: float = WARM_SECONDS, batch: int = 3) -> None:
-    """Run fn() in batches until `seconds` of (synchronised) wall time have passed."""
-    t0 = time.perf_counter()
+def settle(fn, seconds: float = SETTLE_SECONDS, batch: int = 10) -> int:
+    """Call fn(k) in batches until `seconds` of synchronised wall time have
+    passed; returns the number of calls."""
+    t0, calls = time.perf_counter(), 0
     while True:
         for _ in range(batch):
-            fn()
+            fn(calls)
+            calls += 1
         torch.cuda.synchronize()
         if time.perf_counter() - t0 >= seconds:
-            return
+            return calls
 
 
-def time_launches(fn, steps: int) -> float:
-    """Mean seconds per launch of fn() over `steps` launches bracketed by events."""
-    warm_up(fn)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(steps):
-        fn()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) * 1e-3 / steps
+def _call(fn):
+    """fn as a function of the call index (ignored when fn takes none)."""
+    import inspect
+
+    try:
+        takes = len(inspect.signature(fn).parameters) > 0
+    except (TypeError, ValueError):
+        takes = False
+    return fn if takes else (lambda k: fn())
 
 
-def rope_leg(steps: int) -> dict:
+def time_calls(fn, samples: int = SAMPLES, calls: int = CALLS, before_sample=None, join=None) -> dict:
+    """Seconds per call: the median (min, max) over `samples` event pairs, each
+    around `calls` back-to-back calls of fn(k) on the current stream, after a
+    settle period.  before_sample() runs outside the events; join() (if
+    given) makes the current stream wait for work fn queued elsewhere before
+    the closing event."""
+    f = _call(fn)
+    settle(f, WARM_SECONDS, 3)
+    if join:
+        join()
+    out, k = [], 0
+    for _ in range(samples):
+        if before_sample:
+            before_sample()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(calls):
+            f(k)
+            k += 1
+        if join:
+            join()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) * 1e-3 / calls)
+    return {"median_s": float(np.median(out)), "min_s": float(np.min(out)), "max_s": float(np.max(out))}
+
+
+def rope_leg(samples: int) -> dict:
     import row_normalization_amd as rn
 
     w = wl.ROPE1
@@ -288,7 +420,7 @@ def rope_leg(steps: int) -> dict:
     def bwd():
         assert L.rope_bwd(*args) == 0
 
-    t_f, t_b = time_launches(fwd, steps), time_launches(bwd, steps)
+    t_f, t_b = (time_calls(fn, samples)["median_s"] for fn in (fwd, bwd))
     nbytes = wl.rope_algorithmic_bytes(w.tokens, w.heads, w.head_dim, w.elsize, w.seq_len)
     return {"workload": w.name, "fwd_us": round(t_f * 1e6, 2), "bwd_us": round(t_b * 1e6, 2),
             "algorithmic_bytes": nbytes, "fwd_gbps": round(nbytes / t_f / 1e9, 1),
@@ -296,7 +428,7 @@ def rope_leg(steps: int) -> dict:
             "bwd_frac": round(nbytes / t_b / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
-def swiglu_leg(steps: int) -> dict:
+def swiglu_leg(samples: int) -> dict:
     import row_normalization_amd as rn
 
     w = wl.SWIGLU1
@@ -314,7 +446,7 @@ def swiglu_leg(steps: int) -> dict:
         assert L.swiglu_bwd(dh.data_ptr(), e.data_ptr(), g.data_ptr(), h.data_ptr(), df.data_ptr(), de.data_ptr(),
                             w.M, w.N, w.N, code, stream) == 0
 
-    t_f, t_b = time_launches(fwd, steps), time_launches(bwd, steps)
+    t_f, t_b = (time_calls(fn, samples)["median_s"] for fn in (fwd, bwd))
     b = wl.swiglu_algorithmic_bytes(w.M, w.N, w.elsize)
     return {"workload": w.name, "fwd_us": round(t_f * 1e6, 2), "bwd_us": round(t_b * 1e6, 2),
             "fwd_gbps": round(b["fwd"] / t_f / 1e9, 1), "bwd_gbps": round(b["bwd"] / t_b / 1e9, 1),
@@ -322,55 +454,56 @@ def swiglu_leg(steps: int) -> dict:
             "bwd_frac": round(b["bwd"] / t_b / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": b}
 
 
-def time_steps(path: Path, steps: int) -> float:
-    """Seconds per step over `steps` back-to-back steps (HIP events on the stream)."""
+def time_steps(step, steps: int, join=None) -> float:
+    """Seconds per step over exactly `steps` back-to-back steps, bracketed by
+    HIP events on the current stream and device synchronisations."""
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record()
-    for _ in range(steps):
-        path.step()
+    for k in range(steps):
+        step(k)
+    if join:
+        join()
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) * 1e-3 / steps
 
 
-def time_kernels(path, steps: int) -> dict:
-    """Average duration of each launch of the step: `steps` back-to-back
-    launches of that kernel alone, bracketed by one pair of events.
+# Bytes of operand sets rotated through for the "flushed" figures: more than
+# four times the 256 MB Infinity Cache, so a call's operands have always been
+# pushed out by the calls between two uses of the same set.
+ROTATION_BYTES = 1 << 30
 
-    Events recorded between every two launches would each add a marker packet
-    and about 2-6 us of dispatch gap to the launch after it; back to back, the
-    figure agrees with rocprofv3's kernel durations.  Repeating a launch reads
-    and writes the same buffers as the step does (in place, the backward
-    consumes the previous launch's dx as its dy)."""
-    out = {}
-    for name, fn in (("fwd", path.fwd), ("bwd_rows", path.bwd_rows), ("dgamma_reduce", path.reduce)):
-        out[name] = {"mean_s": time_launches(fn, steps)}
+
+def config_protocol(w: wl.Workload, samples: int) -> dict:
+    """Forward, backward (row pass + reduction) and the step of one workload,
+    hot (one operand set) and flushed (sets rotated), medians per call."""
+    b = wl.algorithmic_bytes(w.M, w.N, w.elsize)
+    per_set = (2 if w.dx_in_place else 3) * w.M * w.N * w.elsize + w.M * w.N * w.elsize
+    sets = max(2, -(-ROTATION_BYTES // per_set) + 1)
+    path = Path(w, sets)
+    path.step()
+    torch.cuda.synchronize()
+    out = {"workload": w.name, "M": w.M, "N": w.N, "dtype": w.dtype, "gemma": w.gemma,
+           "dx_in_place": w.dx_in_place, "partial_rows": path.partial_rows, "rotated_sets": sets,
+           "protocol": f"median of {samples} samples x {CALLS} back-to-back calls; in place: dy restored "
+                       "before each sample, outside the events"}
+    legs = {"fwd": (path.fwd, b["fwd"]), "bwd": (path.bwd, b["bwd"]), "step": (path.step, b["fwd_bwd"])}
+    for mode in ("hot", "flushed"):
+        res = {}
+        for leg, (fn, nbytes) in legs.items():
+            f = fn if mode == "flushed" else (lambda k, fn=fn: fn(0))
+            t = time_calls(f, samples, before_sample=path.restore if w.dx_in_place else None)
+            res[leg] = {"us": round(t["median_s"] * 1e6, 2), "min_us": round(t["min_s"] * 1e6, 2),
+                        "gbps": round(nbytes / t["median_s"] / 1e9, 1),
+                        "pct_of_peak": round(100 * nbytes / t["median_s"] / 1e9 / PEAK_HBM_GBPS, 2),
+                        "rows_per_s": round(w.M / t["median_s"], 1)}
+        out[mode] = res
+    print(f"[config] {w.name}: hot step {out['hot']['step']['us']} us ({out['hot']['step']['pct_of_peak']} %), "
+          f"flushed {out['flushed']['step']['us']} us", file=sys.stderr, flush=True)
+    del path
+    torch.cuda.empty_cache()
     return out
-
-
-def time_cold(path: Path, samples: int) -> dict:
-    """Each launch timed alone after a 1 GiB write has pushed the previous data
-    out of L2 and the 256 MB Infinity Cache (medians over `samples`).  Nothing
-    a launch reads is then cached from an earlier launch, except the dgamma
-    partials the row pass has just written for the reduction."""
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(samples)]
-    torch.cuda.synchronize()
-    for k in range(samples):
-        flush.fill_(float(k))
-        ev[k][0].record()
-        path.fwd()
-        ev[k][1].record()
-        flush.fill_(float(k) + 0.5)
-        ev[k][2].record()
-        path.bwd_rows()
-        ev[k][3].record()
-        path.reduce()
-        ev[k][4].record()
-    torch.cuda.synchronize()
-    med = lambda a, b: float(np.median([ev[k][a].elapsed_time(ev[k][b]) * 1e-3 for k in range(samples)]))
-    return {"fwd": med(0, 1), "bwd_rows": med(2, 3), "dgamma_reduce": med(3, 4)}
 
 
 def copy_reference(nbytes: int, steps: int) -> float:
@@ -528,19 +661,34 @@ def main():
     torch.cuda.set_device(0)
     w = wl.RMS_WORKLOADS[args.workload]
     path = Path(w)
-    for _ in range(max(args.warmup, 1)):
-        path.step()
+    overlapped = OverlappedSteps(path)
+    schedules = {"overlapped_reduce": (overlapped.step, overlapped.join), "one_stream": (path.step, None)}
+    step, join = schedules[args.schedule]
+    for k in range(max(args.warmup, 1)):
+        step(k)
+    # then untimed steps until the clocks have settled (a short --warmup alone
+    # leaves the timed steps inside the start-up ramp)
+    settle_steps = settle(step)
+    if join:
+        join()
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
-    sec_per_step = time_steps(path, args.steps)
+    sec_per_step = time_steps(step, args.steps, join)
     wall = time.perf_counter() - t0
-    kern = time_kernels(path, args.steps)
-    cold = time_cold(path, max(10, min(args.steps, 50)))
+    # the other schedule, for context: the same number of steps after its own settle
+    other = "one_stream" if args.schedule == "overlapped_reduce" else "overlapped_reduce"
+    o_step, o_join = schedules[other]
+    settle(o_step)
+    if o_join:
+        o_join()
+    sec_other = time_steps(o_step, args.steps, o_join)
+    kern = {name: time_calls(fn, args.samples)
+            for name, fn in (("fwd", path.fwd), ("bwd_rows", path.bwd_rows), ("dgamma_reduce", path.reduce))}
 
     b = wl.algorithmic_bytes(w.M, w.N, w.elsize)
     value = b["fwd_bwd"] / sec_per_step / 1e9
-    t_rows = kern["bwd_rows"]["mean_s"]
+    t_rows = kern["bwd_rows"]["median_s"]
     achieved = b["bwd_rows"] / t_rows / 1e9
     h = kernel_hash()
     traffic = traffic_from_profile(h)
@@ -552,6 +700,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(sec_per_step * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -559,21 +708,18 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "gemma": w.gemma, "dx_in_place": w.dx_in_place,
-                   "eps": w.eps, "io_dtype": w.dtype, "math": "fp32"},
+                   "eps": w.eps, "io_dtype": w.dtype, "math": "fp32", "schedule": args.schedule},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(w.M / sec_per_step, 1),
         "bytes_per_step": b["fwd_bwd"],
         "wall_s_timed": round(wall, 4),
-        "kernels_us": {k: round(v["mean_s"] * 1e6, 2) for k, v in kern.items()},
-        "kernels_gbps": {"fwd": round(b["fwd"] / kern["fwd"]["mean_s"] / 1e9, 1),
+        "schedules_ms_per_step": {args.schedule: round(sec_per_step * 1e3, 4), other: round(sec_other * 1e3, 4)},
+        "kernels_us": {k: round(v["median_s"] * 1e6, 2) for k, v in kern.items()},
+        "kernels_protocol": f"median of {args.samples} samples x {CALLS} back-to-back launches of the kernel alone",
+        "kernels_gbps": {"fwd": round(b["fwd"] / kern["fwd"]["median_s"] / 1e9, 1),
                          "bwd_rows": round(achieved, 1),
-                         "bwd": round(b["bwd"] / (kern["bwd_rows"]["mean_s"] + kern["dgamma_reduce"]["mean_s"]) / 1e9,
-                                      1)},
-        "cold": {"kernels_us": {k: round(v * 1e6, 2) for k, v in cold.items()},
-                 "ms_per_step": round(sum(cold.values()) * 1e3, 4),
-                 "gbps": round(b["fwd_bwd"] / sum(cold.values()) / 1e9, 1),
-                 "bwd_rows_gbps": round(b["bwd_rows"] / cold["bwd_rows"] / 1e9, 1),
-                 "fwd_gbps": round(b["fwd"] / cold["fwd"] / 1e9, 1)},
+                         "bwd": round(b["bwd"] / (kern["bwd_rows"]["median_s"] + kern["dgamma_reduce"]["median_s"])
+                                      / 1e9, 1)},
         "partial_rows": path.partial_rows,
         "copy_ref_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "rmsnorm_bwd_rows_kernel", "achieved": round(achieved, 1),
@@ -582,19 +728,21 @@ def main():
         "device": device_info(),
         "stream_ceiling": ceiling,
         "kernels_vs_ceiling": None if not ceiling else {
-            "fwd": round(b["fwd"] / kern["fwd"]["mean_s"] / 1e9 / ceiling["read1_write1"]["hot_gbps"], 4),
+            "fwd": round(b["fwd"] / kern["fwd"]["median_s"] / 1e9 / ceiling["read1_write1"]["hot_gbps"], 4),
             "bwd_rows": round(achieved / ceiling["read2_write1"]["hot_gbps"], 4)},
     }
-    del path
+    del overlapped, path, schedules
     torch.cuda.empty_cache()
-    out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_steps, args.ln_ns)
+    out["configs"] = None if args.no_configs else {k: config_protocol(wl.RMS_WORKLOADS[k], args.samples)
+                                                  for k in sorted(wl.RMS_WORKLOADS)}
+    out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_samples, args.ln_ns)
     if args.no_elementwise:
         out["rope"] = out["swiglu"] = None
     else:
-        out["rope"] = rope_leg(100)
+        out["rope"] = rope_leg(args.samples)
         print(f"[rope] {out['rope']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-        out["swiglu"] = swiglu_leg(50)
+        out["swiglu"] = swiglu_leg(args.samples)
         print(f"[swiglu] {out['swiglu']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -20,6 +20,13 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
+// The dtype code (rmsnorm_dtype) of a storage type: float, uint16_t (bf16
+// bits), _Float16.
+template <typename S>
+constexpr int dtype_code() {
+  return sizeof(S) == 4 ? 0 : std::is_same<S, _Float16>::value ? 2 : 1;
+}
+
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family:
 // 32-bit data format; the range check is then offset against the byte count.
 constexpr int kRsrcWord3 = 0x00020000;

@@ -67,7 +67,9 @@ int rope(void* q, int64_t tokens, int64_t heads, int64_t head_dim, int64_t token
   a.nvh = static_cast<int32_t>(half / vec);
   a.items = tokens * a.groups * a.nvh;
   a.sin_sign = sin_sign;
-  if (ceil_div(a.items, kEltThreads) > (int64_t(1) << 31) - 1) return RMSNORM_E_SHAPE;
+  // one thread per item: the launch's work-item count (blocks x threads)
+  // must fit the 32-bit grid size of a dispatch
+  if (ceil_div(a.items, kEltThreads) * kEltThreads > (int64_t(1) << 32) - 1) return RMSNORM_E_SHAPE;
   return hip_status(launch_rope(dtype, vec, a, stream));
 }
 

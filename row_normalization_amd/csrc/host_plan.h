@@ -142,9 +142,83 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
   return found;
 }
 
-// The launch plan of row operation `op` over M rows of N elements of `es`
-// bytes, read in vectors of `vec` elements.
-inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
+// Whether a backward whose rows span 5-8 waves (one row per workgroup of the
+// kBlockWaves-wave shape, two such workgroups per CU) should run one
+// workgroup of two row groups per CU instead: half the partial rows.  Each
+// workgroup writes one fp32 partial row per weight (two for LayerNorm),
+// which the column sum reads back; with `grid` workgroups of the smaller
+// shape that is tables * grid * 4 bytes per column against 3 * M * es of row
+// traffic.  The wide workgroups are taken where that share exceeds
+// kBwdWideShare and the pipelined row loop is compiled for the plan (a single
+// workgroup per CU needs it to keep loads in flight through its barriers).
+// Measured on MI355X (row pass, interleaved comparison): LayerNorm fp16
+// 4096 x 6144 (share 0.17) 10 %, 4096 x 8192 (0.17) 3 %, 16384 x 8192 (0.042)
+// 2 %, fp32 4096 x 4096 (0.083) 3 % and RMSNorm bf16 2048 x 8192 (0.17) 4 %
+// faster; RMSNorm bf16 16384 x 8192 (0.021) 2.3 % and 32768 x 5120 (0.010)
+// 3.7 % slower.  Rows of fewer waves were 3-37 % slower in wide workgroups
+// (4-16 row groups to combine per workgroup), so they keep the smaller shape.
+constexpr double kBwdWideShare = 0.03;
+inline bool bwd_wide_workgroups(RowOp op, int64_t M, int es, int wpr, int64_t grid) {
+  if (wpr * 2 <= kBlockWaves || wpr > kBlockWaves) return false;
+  const int tables = op == RowOp::kLnBwd ? 2 : 1;
+  return static_cast<double>(tables) * static_cast<double>(grid) * 4.0 >
+         kBwdWideShare * 3.0 * static_cast<double>(M) * es;
+}
+
+// Row shapes the rule above does not pick, where an interleaved comparison on
+// MI355X found another shape faster.  An entry applies to the operations in
+// `ops`, elements of `es` bytes (0: either), vectors of `vbytes` bytes (0:
+// any width), rows of lo..hi vectors, and only where the rule's own shape is
+// from_wpr x from_iters; such a row then runs as wpr x iters (waves x vectors
+// per lane).  Every entry stays within the register model (vectors per lane
+// at most the operation's cap for its vector width, checked for all widths
+// by tests/native/plan_check.cpp).
+constexpr unsigned op_bit(RowOp op) { return 1u << static_cast<int>(op); }
+constexpr unsigned kFwdOps = op_bit(RowOp::kRmsFwd) | op_bit(RowOp::kLnFwd);
+constexpr unsigned kBwdOps = op_bit(RowOp::kRmsBwd) | op_bit(RowOp::kLnBwd);
+struct ShapeOverride {
+  unsigned ops;
+  int es, vbytes;
+  int64_t lo, hi;
+  int from_wpr, from_iters, wpr, iters;
+};
+constexpr ShapeOverride kShapeOverrides[] = {
+    // 16-bit forward rows of 129-204 vectors (N = 1032-1632), which the rule
+    // gives 2 waves x 2 with more than a quarter of the vectors empty: one
+    // wave of 4 (no cross-wave sum, eight rows per workgroup).  RMSNorm
+    // 16384 x 1096 16-19 % and 16384 x 1600 7 % faster, LayerNorm 4096 x 1160
+    // 4 % faster, 4096 x 1600 5 % slower; 12-25 % faster than 3 x 1 at N =
+    // 1280 and 1536 (M = 4096 to 65536, both norms).
+    {kFwdOps, 2, 16, 129, 204, 2, 2, 1, 4},
+    // 16-bit forward rows of 308-320 vectors (N = 2464-2560), rule 3 x 2: one
+    // wave of 5, 5-12 % faster at N = 2560.  (Rows of 257-307 vectors get one
+    // wave of 5 from the rule itself; exactly 256 keep 2 x 2, one wave of 4
+    // was up to 12 % slower; 321-384 keep 3 x 2, one wave of 8 or 4 x 2
+    // measured -3 ... +20 %.)
+    {kFwdOps, 2, 16, 308, 320, 3, 2, 1, 5},
+    // 16-bit LayerNorm forward rows of 641-896 vectors (N = 5128-7168), rule
+    // 6 or 7 waves x 2: 3 x 4 or 4 x 4, half the waves in its two cross-wave
+    // sums and a persistent grid from M = 8192 on.  N = 5264, 5896, 6144,
+    // 6432, 7000, 7168: 3.3-10.5 % faster at M = 8192 and 16384, -0.8 ...
+    // +1.3 % at M = 4096.
+    {op_bit(RowOp::kLnFwd), 2, 16, 641, 768, 6, 2, 3, 4},
+    {op_bit(RowOp::kLnFwd), 2, 16, 769, 896, 7, 2, 4, 4},
+    // 16-bit LayerNorm forward rows of 1025-1279 vectors (N = 8200-10232),
+    // rule 5 x 4: 4 x 5, eight-wave workgroups of two rows.  1.4-9.8 %
+    // faster at M = 4096 to 16384 (N = 8704, 9056, 9216); at exactly 1280
+    // vectors (N = 10240, no lane idle in 5 x 4) -2.8 ... +1.6 %, so it keeps
+    // the rule's shape.  RMSNorm's forward measured indifferent (+-1 %).
+    {op_bit(RowOp::kLnFwd), 2, 16, 1025, 1279, 5, 4, 4, 5},
+    // backward rows the rule gives one wave of five vectors (257-320
+    // vectors): 3 x 2, fewer row groups per workgroup to add up at its end.
+    // fp32 RMSNorm N = 1028-1280: 8.6-14 % faster at M = 4096 to 16384.
+    {kBwdOps, 0, 0, 257, 320, 1, 5, 3, 2},
+};
+
+// The launch plan of row operation `op` over M rows of N elements of type
+// `dtype`, read in vectors of `vec` elements.
+inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
+  const int es = elsize(dtype);
   RowPlan p{};
   p.vec = vec;
   const bool backward = op == RowOp::kRmsBwd || op == RowOp::kLnBwd;
@@ -159,55 +233,25 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int es) {
     p.iters = 0;  // cannot happen for N <= RMSNORM_N_MAX
     return p;
   }
-  // 16-bit forward rows of 129-320 vectors (N = 1032-2560) run as one wave
-  // of four or five 16-byte vectors per lane (no cross-wave sum, eight rows
-  // per workgroup) where the rule gives them three waves or more than a
-  // quarter of the covered vectors empty: N = 1032-1632 (2 x 2 with a
-  // partly empty second wave), 2464-2560 (3 x 2); 2056-2456 get one wave
-  // from the rule itself.  Measured on MI355X against 3 x 1 and 3 x 2: 12-25 %
-  // faster at N = 1280 and 1536 (M = 4096 to 65536, both norms), 5-12 % at
-  // N = 2560; against 2 x 2: RMSNorm 16384 x 1096 and 16384 x 1600 16-19 %
-  // and 7 % faster, LayerNorm 4096 x 1160 4 % faster and 4096 x 1600 5 %
-  // slower.  Exactly 256 vectors (N = 2048) keep 2 x 2 (one wave of 4 was up
-  // to 12 % slower), and so do rows of 321-384 (one wave of 8 vectors or
-  // 4 x 2 against 3 x 2: -3 ... +20 %).
-  if (es == 2 && vec * es == 16 && !backward && nvec > 2 * kWave && nvec <= 5 * kWave && cap >= 5 &&
-      (p.wpr == 3 || (int64_t(p.wpr) * p.iters * kWave - nvec) * 4 > nvec)) {
-    p.wpr = 1;
-    p.iters = nvec <= 4 * kWave ? 4 : 5;
-  }
-  // A 16-bit LayerNorm forward row of 1025-1279 vectors (N = 8200-10232),
-  // which the rule gives 5 waves x 4 vectors, runs as 4 x 5: fewer waves in
-  // its two cross-wave sums, and eight-wave workgroups of two rows.  Measured
-  // on MI355X: 1.4-9.8 % faster at M = 4096 to 16384 (N = 8704, 9056, 9216);
-  // at exactly 1280 vectors (N = 10240, no lane idle in 5 x 4) mixed, -2.8
-  // ... +1.6 %, so 5 x 4 stays.
-  if (op == RowOp::kLnFwd && es == 2 && vec == 8 && p.wpr == 5 && p.iters == 4 && nvec < 4 * 5 * kWave &&
-      cap >= 5) {
-    p.wpr = 4;
-    p.iters = 5;
-  }
-  // Likewise 16-bit LayerNorm forward rows the rule gives 6 or 7 waves of two
-  // vectors (N = 5128-7168) run as 3 x 4 or 4 x 4: half the waves, and a
-  // persistent grid from M = 8192 on.  Measured on MI355X (N = 5264, 5896,
-  // 6144, 6432, 7000, 7168): 3.3-10.5 % faster at M = 8192 and 16384,
-  // -0.8 ... +1.3 % at M = 4096.
-  if (op == RowOp::kLnFwd && es == 2 && vec == 8 && p.iters == 2 && (p.wpr == 6 || p.wpr == 7)) {
-    p.wpr = p.wpr == 6 ? 3 : 4;
-    p.iters = 4;
-  }
-  // A backward row the rule gives one wave of five vectors (fp32 RMSNorm,
-  // N = 1028-1280) runs as 3 x 2: fewer row groups per workgroup to add up at
-  // its end.  Measured on MI355X: 8.6-14 % faster over that range at M = 4096
-  // to 16384.
-  if (backward && p.wpr == 1 && p.iters > 4) {
-    p.wpr = static_cast<int>(ceil_div(nvec, 2 * kWave));
-    p.iters = 2;
+  // Shapes measured faster than the rule's choice (the table below).
+  for (const ShapeOverride& o : kShapeOverrides) {
+    if ((o.ops & op_bit(op)) && (o.es == 0 || o.es == es) && (o.vbytes == 0 || o.vbytes == vec * es) &&
+        nvec >= o.lo && nvec <= o.hi && p.wpr == o.from_wpr && p.iters == o.from_iters) {
+      p.wpr = o.wpr;
+      p.iters = o.iters;
+      break;
+    }
   }
   p.rpb = std::max(1, kBlockWaves / p.wpr);
-  const int64_t groups = ceil_div(M, p.rpb);
+  int64_t groups = ceil_div(M, p.rpb);
   int64_t per_cu = 1;
   while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
+  if (backward && bwd_pipeline_fits(op, dtype, p.vec, p.iters) &&
+      bwd_wide_workgroups(op, M, es, p.wpr, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)))) {
+    p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
+    groups = ceil_div(M, p.rpb);
+    per_cu = 1;
+  }
   // The forward is persistent where that grid fills every CU with
   // kBwdResidentWaves waves, or with at least kFwdPersistentMinWaves waves
   // whose lanes each carry four 16-byte vectors, and each workgroup then
@@ -247,8 +291,8 @@ inline int64_t partial_rows_bound(int64_t M) { return std::min(M, kBwdGridMax); 
 // Measured on MI355X (bf16): 8192 x 16384, 8192 x 15872, 16384 x 15360 and
 // 16384 x 9216 row passes 5-9 % faster pipelined; with two workgroups per CU
 // (16384 x 8192, 32768 x 5120) pipelining was 2-8 % slower.
-inline bool bwd_pipelined(const RowPlan& p, int es) {
-  return p.wpr * p.rpb * 2 > kBwdResidentWaves && bwd_pipeline_fits(p.vec, p.iters, es);
+inline bool bwd_pipelined(RowOp op, const RowPlan& p, int dtype) {
+  return p.wpr * p.rpb * 2 > kBwdResidentWaves && bwd_pipeline_fits(op, dtype, p.vec, p.iters);
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_E_HIP; }

@@ -187,11 +187,14 @@ constexpr int lane_elems_cap(RowOp op, int elsize) {
 
 // The backwards' pipelined row loop keeps a second row's x and dy in
 // registers.  It is compiled, and chosen, only where a lane holds at most
-// two 16-byte vectors of each operand (a vector narrower than a register
-// still takes a whole one): beyond that the second row would spill.
-constexpr int kPipelineLaneBytes = 32;
-constexpr bool bwd_pipeline_fits(int vec, int iters, int elsize) {
-  return iters * (vec * elsize > 4 ? vec * elsize : 4) <= kPipelineLaneBytes;
+// two full 16-byte vectors of each operand (beyond that, or with narrower
+// vectors and so more loads and offsets per row, the second row would
+// spill), and not for the bf16 LayerNorm backward: its third per-column
+// table (the db partials) and bf16's unpacking take ~140 registers with two
+// rows in flight, past the 128 a lane of a 16-wave workgroup has.
+constexpr int kPipelineLaneVectors = 2;
+constexpr bool bwd_pipeline_fits(RowOp op, int dtype, int vec, int iters) {
+  return vec * (dtype == 0 ? 4 : 2) == 16 && iters <= kPipelineLaneVectors && !(op == RowOp::kLnBwd && dtype == 1);
 }
 
 // Tile of the dgamma reduction: kReduceCols column threads (a 128-byte row

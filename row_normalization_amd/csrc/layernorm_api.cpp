@@ -57,7 +57,7 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
                                const float* rstd, void* dx, void* workspace, int64_t M, int64_t N, int64_t stride,
                                int dtype, int64_t* rows_written, hipStream_t stream) {
   const int vec = choose_vec(dtype, N, stride, {x, weight, dy, dx});
-  const RowPlan p = plan_rows(RowOp::kLnBwd, M, N, vec, elsize(dtype));
+  const RowPlan p = plan_rows(RowOp::kLnBwd, M, N, vec, dtype);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnBwdArgs a{};
   a.x = x;
@@ -75,7 +75,7 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
-  a.pipeline = bwd_pipelined(p, elsize(dtype));
+  a.pipeline = bwd_pipelined(RowOp::kLnBwd, p, dtype);
   const int st = hip_status(launch_ln_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;
   return st;
@@ -115,7 +115,7 @@ int layernorm_fwd(const void* x, const void* weight, const void* bias, void* y, 
   if (overlap(sy, sm) || overlap(sy, sr) || overlap(sm, sr)) return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, weight, bias, y});
-  const RowPlan p = plan_rows(RowOp::kLnFwd, M, N, vec, elsize(dtype));
+  const RowPlan p = plan_rows(RowOp::kLnFwd, M, N, vec, dtype);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnFwdArgs a{};
   a.x = x;
@@ -158,7 +158,8 @@ int layernorm_bwd_rows(const void* x, const void* weight, const void* dy, const 
 }
 
 int layernorm_dwdb_reduce(const float* partials, int64_t rows, int64_t N, float* dw, float* db, hipStream_t stream) {
-  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX || 2 * rows * N > RMSNORM_PARTIALS_MAX) return RMSNORM_E_SHAPE;
+  // two tables of rows x N; bounded by division, as 2 * rows * N could wrap
+  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX || rows > RMSNORM_PARTIALS_MAX / (2 * N)) return RMSNORM_E_SHAPE;
   if (!dw || !db || (rows > 0 && !partials)) return RMSNORM_E_NULL;
   if (!aligned(dw, 4) || !aligned(db, 4) || (rows > 0 && !aligned(partials, 4))) return RMSNORM_E_ALIGN;
   const Span sp = span(partials, 2 * rows * N * 4), sw = span(dw, N * 4), sb = span(db, N * 4);

@@ -266,20 +266,23 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
   }
 
   bool pipelined = false;
-  if constexpr (bwd_pipeline_fits(VEC, ITERS, sizeof(S))) pipelined = a.pipeline;
+  if constexpr (bwd_pipeline_fits(RowOp::kLnBwd, dtype_code<S>(), VEC, ITERS)) pipelined = a.pipeline;
   if (pipelined) {
-    // One workgroup per CU: the next row's loads are issued before this
-    // row's sums, barrier and stores (as in the RMSNorm backward).
+    // One workgroup per CU: the next row's loads are in flight during this
+    // row's sums, barrier and stores.  Unconditional loads over an even
+    // number of steps and scheduling barriers between the rows, for the
+    // reasons given in the RMSNorm backward (rows past M load zeros, store
+    // nothing and add nothing to the partials).
     LnBwdRow<S, VEC, ITERS> ta, tb;
     ln_bwd_load_row(ta, a, 0, L, G);
+    __builtin_amdgcn_sched_barrier(0);
     for (int64_t step = 0; step < a.row_iters; step += 2) {
-      const bool has_b = step + 1 < a.row_iters;
-      if (has_b) ln_bwd_load_row(tb, a, step + 1, L, G);
+      ln_bwd_load_row(tb, a, step + 1, L, G);
+      __builtin_amdgcn_sched_barrier(0);
       ln_bwd_process_row(ta, a, step, w, accw, accb, red, L, G);
-      if (has_b) {
-        if (step + 2 < a.row_iters) ln_bwd_load_row(ta, a, step + 2, L, G);
-        ln_bwd_process_row(tb, a, step + 1, w, accw, accb, red, L, G);
-      }
+      ln_bwd_load_row(ta, a, step + 2, L, G);
+      __builtin_amdgcn_sched_barrier(0);
+      ln_bwd_process_row(tb, a, step + 1, w, accw, accb, red, L, G);
     }
   } else {
     // One row at a time.  This loop carries the same row work as

@@ -54,11 +54,16 @@ int check_bwd(const void* x, const void* gamma, const void* dy, const float* rst
   return RMSNORM_OK;
 }
 
+RowPlan bwd_plan(const void* x, const void* gamma, const void* dy, const void* dx, int64_t M, int64_t N,
+                 int64_t stride, int dtype) {
+  const int vec = choose_vec(dtype, N, stride, {x, gamma, dy, dx});
+  return plan_rows(RowOp::kRmsBwd, M, N, vec, dtype);
+}
+
 int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx,
                             void* workspace, int64_t M, int64_t N, int64_t stride, int dtype, int flags,
                             int64_t* rows_written, hipStream_t stream) {
-  const int vec = choose_vec(dtype, N, stride, {x, gamma, dy, dx});
-  const RowPlan p = plan_rows(RowOp::kRmsBwd, M, N, vec, elsize(dtype));
+  const RowPlan p = bwd_plan(x, gamma, dy, dx, M, N, stride, dtype);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   BwdArgs a{};
   a.x = x;
@@ -70,13 +75,13 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
   a.M = M;
   a.stride = stride;
   a.N = static_cast<int32_t>(N);
-  a.nvec = static_cast<int32_t>(N / vec);
+  a.nvec = static_cast<int32_t>(N / p.vec);
   a.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
   a.w_off = (flags & RMSNORM_GEMMA) ? 1.0f : 0.0f;
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
-  a.pipeline = bwd_pipelined(p, elsize(dtype));
+  a.pipeline = bwd_pipelined(RowOp::kRmsBwd, p, dtype);
   const int st = hip_status(launch_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;
   return st;
@@ -110,7 +115,7 @@ int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t 
     return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, gamma, y});
-  const RowPlan p = plan_rows(RowOp::kRmsFwd, M, N, vec, elsize(dtype));
+  const RowPlan p = plan_rows(RowOp::kRmsFwd, M, N, vec, dtype);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   FwdArgs a{};
   a.x = x;
@@ -154,7 +159,8 @@ int rmsnorm_bwd_rows(const void* x, const void* gamma, const void* dy, const flo
 }
 
 int rmsnorm_dgamma_reduce(const float* partials, int64_t rows, int64_t N, float* dgamma, hipStream_t stream) {
-  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX || rows * N > RMSNORM_PARTIALS_MAX) return RMSNORM_E_SHAPE;
+  // the table bound is tested by division: rows * N could wrap for huge rows
+  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX || rows > RMSNORM_PARTIALS_MAX / N) return RMSNORM_E_SHAPE;
   if (!dgamma || (rows > 0 && !partials)) return RMSNORM_E_NULL;
   if (!aligned(dgamma, 4) || (rows > 0 && !aligned(partials, 4))) return RMSNORM_E_ALIGN;
   if (rows > 0 && overlap(span(partials, rows * N * 4), span(dgamma, N * 4))) return RMSNORM_E_ALIAS;

@@ -248,22 +248,29 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
   }
 
   bool pipelined = false;
-  if constexpr (bwd_pipeline_fits(VEC, ITERS, sizeof(S))) pipelined = a.pipeline;
+  if constexpr (bwd_pipeline_fits(RowOp::kRmsBwd, dtype_code<S>(), VEC, ITERS)) pipelined = a.pipeline;
   if (pipelined) {
-    // One workgroup per CU: the next row's loads are issued before this
+    // One workgroup per CU: the next row's loads are in flight during this
     // row's reduction, barrier and stores, so the memory system is not idle
     // while they run.  Rows are still processed in order (the LDS slots of
-    // the row sums alternate by step).
+    // the row sums alternate by step).  Every load is unconditional: steps
+    // past the last one hold only rows past M, whose loads read zero and
+    // whose stores are dropped (and whose zero operands add nothing to the
+    // partials), so the trip count can be even and the compiler sees the
+    // same memory operations on every trip.  It then waits for exactly the
+    // row it is about to use; a load under a condition made it wait for every
+    // operation in flight, the next row's loads included.  The scheduling
+    // barriers keep each row's arithmetic below the previous row's stores.
     BwdRow<S, VEC, ITERS> tb;
     bwd_load_row(ta, a, 0, L, G);
+    __builtin_amdgcn_sched_barrier(0);
     for (int64_t step = 0; step < a.row_iters; step += 2) {
-      const bool has_b = step + 1 < a.row_iters;
-      if (has_b) bwd_load_row(tb, a, step + 1, L, G);
+      bwd_load_row(tb, a, step + 1, L, G);
+      __builtin_amdgcn_sched_barrier(0);
       bwd_process_row(ta, a, step, w, acc, red, L, G);
-      if (has_b) {
-        if (step + 2 < a.row_iters) bwd_load_row(ta, a, step + 2, L, G);
-        bwd_process_row(tb, a, step + 1, w, acc, red, L, G);
-      }
+      bwd_load_row(ta, a, step + 2, L, G);
+      __builtin_amdgcn_sched_barrier(0);
+      bwd_process_row(tb, a, step + 1, w, acc, red, L, G);
     }
   } else {
     // One row at a time: with two workgroups per CU the other workgroup's

@@ -8,8 +8,10 @@
 // tests/test_host_contract.py with AddressSanitizer and UndefinedBehavior-
 // Sanitizer, which also watch the validation arithmetic itself.  Prints one
 // summary line and exits non-zero on any failure.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
+#include <limits>
 #include <initializer_list>
 
 #include "host_plan.h"
@@ -70,7 +72,7 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
   ++g_launches;
   check_row_plan(p, RowOp::kRmsBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 4 <= 65536, "LDS combine size", a.N);
-  expect(!a.pipeline || (bwd_pipeline_fits(p.vec, p.iters, elsize_of(dtype)) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
+  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kRmsBwd, dtype, p.vec, p.iters) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
          "pipelined only where it fits and one workgroup fills the CU");
   expect(p.grid <= partial_rows_bound(a.M), "partial rows within the workspace", p.grid);
   return hipSuccess;
@@ -93,7 +95,7 @@ hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, h
   ++g_launches;
   check_row_plan(p, RowOp::kLnBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 8 <= 65536, "LDS combine size", a.N);
-  expect(!a.pipeline || (bwd_pipeline_fits(p.vec, p.iters, elsize_of(dtype)) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
+  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kLnBwd, dtype, p.vec, p.iters) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
          "pipelined only where it fits and one workgroup fills the CU");
   return hipSuccess;
 }
@@ -104,7 +106,8 @@ hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t) {
   expect(a.nvh * vec == a.half, "rope vectors per half");
   expect(a.groups == (a.heads + kRopeGroup - 1) / kRopeGroup, "rope head groups");
   expect(a.items == a.tokens * a.groups * a.nvh, "rope items");
-  expect((a.items + kEltThreads - 1) / kEltThreads <= (int64_t(1) << 31) - 1, "rope grid");
+  expect((a.items + kEltThreads - 1) / kEltThreads * kEltThreads <= (int64_t(1) << 32) - 1,
+         "rope work items fit a dispatch");
   expect(a.table_rows * a.half * 4 < (int64_t(1) << 31), "table descriptor range");
   expect(int64_t(a.heads) * a.half * 2 * es < (int64_t(1) << 31), "token descriptor range");
   expect(a.sin_sign == 1.0f || a.sin_sign == -1.0f, "rope direction");
@@ -204,6 +207,18 @@ int main() {
         for (int64_t D : {2, 6, 64, 128, 256, 1024})
           for (int64_t extra : {int64_t(0), 2 * H * D}) {
             const int64_t stride = H * D + extra;
+            // one thread per (token, group of four heads, vector of the half-head):
+            // calls of more work items than a dispatch holds (2^32 - 1) are rejected
+            const int64_t vec = std::min<int64_t>(16 / elsize_of(dtype), D / 2 & -(D / 2));
+            const int64_t items = T * ((H + rmsn::kRopeGroup - 1) / rmsn::kRopeGroup) * (D / 2 / vec);
+            if ((items + rmsn::kEltThreads - 1) / rmsn::kEltThreads * rmsn::kEltThreads > (int64_t(1) << 32) - 1) {
+              const int64_t before = g_launches;
+              expect(rope_fwd(slot(0), T, H, D, stride, reinterpret_cast<const float*>(slot(1)),
+                              reinterpret_cast<const float*>(slot(2)), 4096, nullptr, 2048, dtype,
+                              nullptr) == RMSNORM_E_SHAPE && g_launches == before,
+                     "rope beyond one dispatch rejected", T, H * D);
+              continue;
+            }
             for (bool with_positions : {false, true}) {
               const int32_t* pos = with_positions ? reinterpret_cast<const int32_t*>(slot(3)) : nullptr;
               expect_ok(rope_fwd(slot(0), T, H, D, stride, reinterpret_cast<const float*>(slot(1)),
@@ -229,6 +244,20 @@ int main() {
           expect_ok(swiglu_bwd(slot(3), slot(0), slot(1), slot(3), slot(0), slot(1), M, N, stride, dtype, nullptr),
                     "swiglu_bwd in place", M, N);
         }
+
+  // reductions of tables whose element count would wrap int64: rejected, nothing launched
+  const long launches_before = g_launches;
+  for (int64_t rows : {int64_t(1) << 61, int64_t(1) << 62, std::numeric_limits<int64_t>::max()})
+    for (int64_t N : {int64_t(1), int64_t(4), int64_t(8), int64_t(16384)}) {
+      expect(rmsnorm_dgamma_reduce(reinterpret_cast<const float*>(slot(6)), rows, N,
+                                   reinterpret_cast<float*>(slot(7)), nullptr) == RMSNORM_E_SHAPE,
+             "huge rmsnorm partials table rejected", rows, N);
+      expect(layernorm_dwdb_reduce(reinterpret_cast<const float*>(slot(6)), rows, N,
+                                   reinterpret_cast<float*>(slot(7)), reinterpret_cast<float*>(slot(10)),
+                                   nullptr) == RMSNORM_E_SHAPE,
+             "huge layernorm partials tables rejected", rows, N);
+    }
+  expect(g_launches == launches_before, "no launch for a rejected table");
 
   std::printf("%ld launches checked, %ld checks, %ld bad\n", g_launches, g_checks, g_bad);
   return g_bad ? 1 : 0;

@@ -32,7 +32,7 @@ static int print_widths() {
       for (int vec = 16 / es; vec >= 1; vec /= 2)
         for (int64_t N = vec; N <= RMSNORM_N_MAX; N += vec) {
           if (vec < 16 / es && N % (2 * vec) == 0) continue;  // N alone would allow a wider vector
-          const RowPlan p = plan_rows(op, 33, N, vec, es);
+          const RowPlan p = plan_rows(op, 33, N, vec, es == 4 ? 0 : 1);
           const auto key = std::make_tuple(static_cast<int>(op), es, vec, p.wpr, p.iters);
           auto it = first_last.find(key);
           if (it == first_last.end())
@@ -61,7 +61,7 @@ int main(int argc, char** argv) {
           if (N % vec) continue;
           const bool bwd = op == RowOp::kRmsBwd || op == RowOp::kLnBwd;
           for (int64_t M : {int64_t(1), int64_t(4096), int64_t(1) << 20}) {
-            const RowPlan p = plan_rows(op, M, N, vec, elsize(dt));
+            const RowPlan p = plan_rows(op, M, N, vec, dt);
             ++n;
             const int64_t lds = p.rpb > 1 ? (op == RowOp::kLnBwd ? 8 : 4) * N : 0;
             const bool ok = p.iters > 0 && p.vec * p.iters <= lane_elems_cap(op, elsize(dt)) && p.threads() <= 1024 &&
@@ -102,7 +102,7 @@ int main(int argc, char** argv) {
       {4, 3328, RowOp::kRmsFwd, 7, 2},                                        // not 13 x 1
   };
   for (const Pin& q : pins) {
-    const RowPlan p = plan_rows(q.op, 4096, q.N, 16 / q.es, q.es);
+    const RowPlan p = plan_rows(q.op, 4096, q.N, 16 / q.es, q.es == 4 ? 0 : 1);
     ++n;
     if (p.wpr != q.wpr || p.iters != q.iters) {
       ++bad;

@@ -26,13 +26,12 @@ dx is the difference of two terms, r*u and x*r^3*m.  Where they cancel (a
 row of one column, N = 1, is the extreme: dx = r*u*eps/(x^2 + eps)), fp32
 evaluation of the difference leaves an absolute error of a few units in the
 last place of r*u no matter how the kernel is written.  dx's bounds therefore
-get an allowance proportional to the oracle's direct term |r*u|: 2^-20 |r u|
-per element for fp32 (eight fp32 ulps: the roundings of r*u, of r^3 * m and of
-the fused difference make about three, and rsqrt's error of up to one ulp in
-r reaches dx = r*u*(1 - x^2 r^2) twice over, since d dx / d r ~ -2u there; at
-N = 1 an rsqrt one ulp low gives 2.2 ulps) and 2^-18 ||r u|| in the bf16
-norm-wise bound.  Away from cancellation |r u| ~ |dx| and the allowance is
-below 1e-5 of the bound; a dropped r^3 term still misses by ~1e-2.
+get an allowance proportional to the oracle's direct term |r*u| (``TOL``:
+eight fp32 ulps of |r u| per element for fp32, 2^-18 ||r u|| in the 16-bit
+norm-wise bound, both set by the units of ``check_close``'s ``direct``).  Away from cancellation |r u| ~ |dx| and the allowance is
+below 1e-5 of the bound; a dropped r^3 term still misses by ~1e-2.  fp32
+outputs must also meet the plain relative error |g - o| / |o| <= eps on the
+elements of at least a tenth of rms(o) whose allowance is negligible.
 """
 from __future__ import annotations
 
@@ -43,37 +42,101 @@ import oracle
 import row_normalization_amd as rn
 import workloads as wl
 
+# Every bound the RMSNorm parity tests apply, with its source.  The values are
+# frozen: tests/test_tolerances.py pins each one, so that a change of a bound
+# is an edit of that test as well, made with its reason.
+TOL = {
+    # the stated parity bar for fp32 I/O (max relative error on y, dx; dgamma)
+    "f32_y": 1e-5,
+    "f32_dx": 1e-5,
+    "f32_dgamma": 1e-4,
+    # the stated bar for 16-bit I/O: dgamma accumulated in fp32, 1e-3 relative
+    "16bit_dgamma": 1e-3,
+    # the stated bf16 rule "max abs 2e-2 plus relative 1.6e-2", read as allclose
+    "bf16_atol": 2e-2,
+    "bf16_rtol": 1.6e-2,
+    # the RMSNorm tutorial's fp16 rule (its "Ba so sánh số học riêng biệt":
+    # allclose with atol = rtol = 3e-3)
+    "f16_atol": 3e-3,
+    "f16_rtol": 3e-3,
+    # norm-wise guard for 16-bit y and dx (the allclose bound is loose next to
+    # the dx projection term): an fp32-in-bf16-out emulation of the kernel on
+    # the headline distributions gave 1.7e-3 with the method intact and
+    # 1.1e-2 with the r^3 term dropped
+    "16bit_normwise": 4e-3,
+    # 16-bit dx row invariant sum_j dx_ij x_ij ~ 0, median over rows of
+    # |sum dx x| / (||dx|| ||x||): 1.3e-5 intact, 7.8e-3 with the r^3 term
+    # dropped in the same emulation
+    "dx_invariant": 1e-3,
+    # r against the oracle's: fp32 sum of N squares and rsqrt within one ulp
+    "rstd_rel": 2e-6,
+    # Cancellation allowances: a caller passes the oracle's direct term (the
+    # larger of the two terms whose difference is the output, e.g. |r u| for
+    # RMSNorm dx); fp32 outputs may then be off by this many units of it per
+    # element (2^-22: two fp32 ulps, the final rounding of the difference and
+    # of its larger operand) ...
+    "f32_direct_units": 2.0**-22,
+    # ... and 16-bit outputs by this many units of its norm in the norm-wise
+    # bound
+    "16bit_direct_units": 2.0**-20,
+    # RMSNorm dx passes four times |r u|, eight fp32 ulps in all: the
+    # roundings of r*u, r^3*m and the fused difference make about three, and
+    # rsqrt's error of up to one ulp in r reaches dx = r u (1 - x^2 r^2) twice
+    # over; an N = 1 row with rsqrt one ulp low gave 2.2 ulps on the GPU, and
+    # the same on the CPU in fp32 with r one ulp below the rounded value
+    "rms_dx_direct_multiple": 4.0,
+    # where the plain relative error |g - o| / |o| is also required: elements
+    # of at least this fraction of rms(o), whose allowance is below a tenth
+    # of the bound
+    "plain_floor": 0.1,
+}
+
 
 def check_close(name: str, g: np.ndarray, o: np.ndarray, dtype: str, kind: str, direct=None) -> dict:
     """Assert the tolerance rule for one output; returns diagnostics.
 
-    ``direct`` (dx only): the oracle's r*u, the scale of the fp32 cancellation allowance.
+    ``direct``: the oracle's direct term where the output is a difference
+    that can cancel (per element), or None; it sets the allowance of
+    ``TOL["f32_direct_units"]`` (fp32, per element) or
+    ``TOL["16bit_direct_units"]`` (16-bit, norm-wise) units of it.
     """
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
-    direct = np.zeros_like(o) if direct is None else np.abs(np.asarray(direct, np.float64))
+    units = TOL["f32_direct_units"] if dtype == "f32" or kind == "dgamma" else TOL["16bit_direct_units"]
+    allow = np.zeros_like(o) if direct is None else units * np.abs(np.asarray(direct, np.float64))
     assert g.shape == o.shape, (name, g.shape, o.shape)
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
     diag = {}
     if o.size == 0:
         return diag
     if dtype == "f32" or kind == "dgamma":
-        eps = {"y": 1e-5, "dx": 1e-5, "dgamma": 1e-4 if dtype == "f32" else 1e-3}[kind]
-        scale = np.abs(o) + np.sqrt(np.mean(o * o))
-        rel = np.abs(g - o) / np.where(scale == 0, 1.0, scale)
-        rel = np.where(np.abs(g - o) <= 2.0**-22 * direct, 0.0, rel)
+        eps = {"y": TOL["f32_y"], "dx": TOL["f32_dx"],
+               "dgamma": TOL["f32_dgamma"] if dtype == "f32" else TOL["16bit_dgamma"]}[kind]
+        rms = np.sqrt(np.mean(o * o))
+        scale = np.abs(o) + rms
+        err = np.abs(g - o)
+        rel = err / np.where(scale == 0, 1.0, scale)
+        rel = np.where(err <= allow, 0.0, rel)
         worst = np.unravel_index(np.argmax(rel), rel.shape)
         diag["max_rel"] = float(rel.max())
         assert rel.max() <= eps, f"{name}: max rel err {rel.max():.3g} > {eps} at {worst}: {g[worst]} vs {o[worst]}"
+        # plain relative error where it is well posed: away from cancellation
+        away = (np.abs(o) > 0) & (np.abs(o) >= TOL["plain_floor"] * rms) & (allow <= 0.1 * eps * np.abs(o))
+        if away.any():
+            plain = err[away] / np.abs(o[away])
+            diag["plain_rel"] = float(plain.max())
+            assert plain.max() <= eps, f"{name}: plain rel err {plain.max():.3g} > {eps} (|o| >= 0.1 rms)"
     else:
-        bound = 2e-2 + 1.6e-2 * np.abs(o) if dtype == "bf16" else 3e-3 + 3e-3 * np.abs(o)
+        atol, rtol = ((TOL["bf16_atol"], TOL["bf16_rtol"]) if dtype == "bf16" else (TOL["f16_atol"], TOL["f16_rtol"]))
+        bound = atol + rtol * np.abs(o)
         err = np.abs(g - o)
         worst = np.unravel_index(np.argmax(err - bound), err.shape)
         assert np.all(err <= bound), f"{name}: |g-o| {err[worst]:.3g} > {bound[worst]:.3g} at {worst}"
         e2, o2 = np.linalg.norm(g - o), np.linalg.norm(o)
         nrm = e2 / max(o2, 1e-300)
         diag["normwise"] = float(nrm)
-        assert e2 <= 4e-3 * o2 + 2.0**-20 * np.linalg.norm(direct), f"{name}: norm-wise error {nrm:.3g} > 4e-3"
+        assert e2 <= TOL["16bit_normwise"] * o2 + np.linalg.norm(allow), \
+            f"{name}: norm-wise error {nrm:.3g} > {TOL['16bit_normwise']}"
     return diag
 
 
@@ -86,13 +149,13 @@ def check_dx_invariant(name: str, dx: np.ndarray, x: np.ndarray) -> float:
         return 0.0
     res = np.abs(np.sum(dx * x, axis=1))[ok] / (nx[ok] * nd[ok])
     med = float(np.median(res))
-    assert med <= 1e-3, f"{name}: row invariant residual median {med:.3g} > 1e-3"
+    assert med <= TOL["dx_invariant"], f"{name}: row invariant residual median {med:.3g} > {TOL['dx_invariant']}"
     return med
 
 
 def check_rstd(name: str, r_gpu: np.ndarray, r_orc: np.ndarray) -> None:
     rel = np.abs(r_gpu - r_orc) / r_orc
-    assert rel.max() <= 2e-6, f"{name}: rstd rel err {rel.max():.3g} at row {int(np.argmax(rel))}"
+    assert rel.max() <= TOL["rstd_rel"], f"{name}: rstd rel err {rel.max():.3g} at row {int(np.argmax(rel))}"
 
 
 def padded(t: torch.Tensor, row_stride: int, fill: float, offset: int = 0) -> torch.Tensor:
@@ -151,8 +214,8 @@ def compare_with_oracle(run: Run, rows: np.ndarray | None = None) -> dict:
     diag = {}
     diag["y"] = check_close(f"{w.name} y", y[sel], y_o[sel], w.dtype, "y")
     check_rstd(f"{w.name} rstd", r[sel], r_o[sel])
-    # check_close allows 2^-22 * direct: four times |r u| makes 2^-20 |r u|
-    direct = 4.0 * r_o[:, None] * dy * oracle.weight(gamma, w.gemma)[None, :]
+    # the direct term |r u| of dx = r u - x r^3 m, scaled to eight fp32 ulps
+    direct = TOL["rms_dx_direct_multiple"] * np.abs(r_o[:, None] * dy * oracle.weight(gamma, w.gemma)[None, :])
     diag["dx"] = check_close(f"{w.name} dx", dx[sel], dx_o[sel], w.dtype, "dx", direct=direct[sel])
     if w.dtype != "f32" and w.N >= 64:
         diag["dx_invariant"] = check_dx_invariant(f"{w.name} dx", dx[sel], x[sel])

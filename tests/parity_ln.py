@@ -42,13 +42,38 @@ import workloads as wl
 from oracle import layernorm_oracle as lo
 from tests.parity import check_close, padded
 
+# The LayerNorm-specific bounds (y, dx, dw, db otherwise take check_close's
+# per-dtype rules), each with its source; frozen like those of
+# tests/parity.py (tests/test_tolerances.py pins them).
+TOL_LN = {
+    # mean: fp32 rounding of a sum of N values, relative to |mean| + the
+    # row's spread (sqrt(var + eps)); sums of 16384 unit-spread values in fp32
+    # on the CPU stay below 3e-7
+    "mean_rel": 2e-6,
+    # rstd: a second fp32 sum, over the squared differences from the fp32
+    # mean, then rsqrt within one ulp
+    "rstd_rel": 4e-6,
+    # 16-bit dx rows sum to zero (LayerNorm's shift invariance): median over
+    # rows of |sum_j dx_ij| / (||dx_i|| sqrt(N)); a dropped c2 term fails it
+    # by orders of magnitude
+    "row_sums": 1e-3,
+    # dw's centering allowance: the rows' fp32 centering errors (one ulp of
+    # max|x| of the row, times rstd) reach dw through dy; independent between
+    # rows, so they add as a root sum of squares, allowed four fp32 ulps of it
+    # (2^-20 with check_close's 2^-22 units).  Near-constant rows x = 5 +
+    # 1e-3 z (|mean| / sigma = 5000) need it: at N = 2 dw was off by 1.5e-4
+    # relative on the GPU, and an fp32 evaluation in the kernel's order on the
+    # CPU gave the same value
+    "dw_center_factor": 4.0,
+}
+
 
 def check_mean_rstd(name: str, mean_g, rstd_g, mean_o, rstd_o) -> None:
     sd = 1.0 / rstd_o  # sqrt(var + eps) >= sqrt(var)
     err_m = np.abs(mean_g - mean_o) / (np.abs(mean_o) + sd)
-    assert err_m.max() <= 2e-6, f"{name}: mean err {err_m.max():.3g} at row {int(np.argmax(err_m))}"
+    assert err_m.max() <= TOL_LN["mean_rel"], f"{name}: mean err {err_m.max():.3g} at row {int(np.argmax(err_m))}"
     rel = np.abs(rstd_g - rstd_o) / rstd_o
-    assert rel.max() <= 4e-6, f"{name}: rstd rel err {rel.max():.3g} at row {int(np.argmax(rel))}"
+    assert rel.max() <= TOL_LN["rstd_rel"], f"{name}: rstd rel err {rel.max():.3g} at row {int(np.argmax(rel))}"
 
 
 def check_row_sums_vanish(name: str, dx: np.ndarray) -> float:
@@ -58,7 +83,7 @@ def check_row_sums_vanish(name: str, dx: np.ndarray) -> float:
         return 0.0
     res = np.abs(dx.sum(axis=1))[ok] / (nd[ok] * np.sqrt(dx.shape[1]))
     med = float(np.median(res))
-    assert med <= 1e-3, f"{name}: row sums of dx: median residual {med:.3g} > 1e-3"
+    assert med <= TOL_LN["row_sums"], f"{name}: row sums of dx: median residual {med:.3g} > {TOL_LN['row_sums']}"
     return med
 
 
@@ -132,7 +157,8 @@ def compare_ln_with_oracle(run: LnRun, rows: np.ndarray | None = None) -> dict:
         # each row's fp32 centering error, carried by dy * x_hat into the column
         # sums; independent between rows, so combined as a root sum of squares
         _, _, r_all = lo.forward(x, wt, b, w.eps)
-        dw_center = 4.0 * np.sqrt(np.sum((dy * (np.max(np.abs(x), axis=1) * r_all)[:, None]) ** 2, axis=0))
+        dw_center = TOL_LN["dw_center_factor"] * np.sqrt(
+            np.sum((dy * (np.max(np.abs(x), axis=1) * r_all)[:, None]) ** 2, axis=0))
     diag["dw"] = check_close(f"{w.name} dw", dw_g, dw_o, w.dtype, "dgamma", direct=dw_center)
     diag["db"] = check_close(f"{w.name} db", db_g, db_o, w.dtype, "dgamma")
     return diag

@@ -164,6 +164,12 @@ def test_dgamma_reduce_rejections(L):
     assert L.rmsnorm_dgamma_reduce(WS, -1, 8, DG, None) == E_SHAPE
     assert L.rmsnorm_dgamma_reduce(WS, 4, 0, DG, None) == E_SHAPE
     assert L.rmsnorm_dgamma_reduce(WS, 4, 16385, DG, None) == E_SHAPE
+    # tables beyond RMSNORM_PARTIALS_MAX floats, including row counts whose
+    # product with N wraps around int64 (1 << 62 rows x 4 columns wraps to 0)
+    assert L.rmsnorm_dgamma_reduce(WS, (1 << 29) // 8 + 1, 8, DG, None) == E_SHAPE
+    assert L.rmsnorm_dgamma_reduce(WS, 1 << 62, 4, DG, None) == E_SHAPE
+    assert L.rmsnorm_dgamma_reduce(WS, 1 << 61, 8, DG, None) == E_SHAPE
+    assert L.rmsnorm_dgamma_reduce(WS, (1 << 63) - 1, 16384, DG, None) == E_SHAPE
     assert L.rmsnorm_dgamma_reduce(WS, 4, 8, None, None) == E_NULL
     assert L.rmsnorm_dgamma_reduce(None, 4, 8, DG, None) == E_NULL
     assert L.rmsnorm_dgamma_reduce(WS + 1, 4, 8, DG, None) == E_ALIGN

@@ -41,6 +41,11 @@ def test_rope_rejections(L, fn):
     assert rope(L, fn, H=(1 << 24) // 128 + 1) == E_SHAPE   # heads * head_dim > 2^24
     assert rope(L, fn, H=1 << 62, stride=1 << 40) == E_SHAPE  # no overflow in heads * head_dim
     assert rope(L, fn, stride=1 << 61) == E_SHAPE           # byte offsets beyond int64
+    # one thread per (token, 4-head group, 16-byte vector): 2^29 tokens of 4
+    # heads x 128 bf16 make 2^32 work items, one more than a dispatch holds
+    far = dict(q=1 << 44, cos=1 << 45, sin=(1 << 45) + GiB, pos=1 << 46)
+    assert rope(L, fn, T=1 << 29, **far) == E_SHAPE
+    assert rope(L, fn, T=1 << 29, H=8, **far) == E_SHAPE
     for kw in ("q", "cos", "sin"):
         assert rope(L, fn, **{kw: None}) == E_NULL, kw
     assert rope(L, fn, q=Q + 1) == E_ALIGN

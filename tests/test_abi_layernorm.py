@@ -128,6 +128,10 @@ def test_dwdb_reduce_rejections(L):
     assert L.layernorm_dwdb_reduce(WS, -1, 8, DW, DB, None) == E_SHAPE
     assert L.layernorm_dwdb_reduce(WS, 4, 0, DW, DB, None) == E_SHAPE
     assert L.layernorm_dwdb_reduce(WS, 1 << 15, 1 << 14, DW, DB, None) == E_SHAPE  # 2 * rows * N > 2^29
+    # row counts whose 2 * rows * N wraps around int64 (to 0 for 1 << 61 rows x 4)
+    assert L.layernorm_dwdb_reduce(WS, 1 << 61, 4, DW, DB, None) == E_SHAPE
+    assert L.layernorm_dwdb_reduce(WS, 1 << 62, 4, DW, DB, None) == E_SHAPE
+    assert L.layernorm_dwdb_reduce(WS, (1 << 63) - 1, 16384, DW, DB, None) == E_SHAPE
     assert L.layernorm_dwdb_reduce(WS, 4, 8, None, DB, None) == E_NULL
     assert L.layernorm_dwdb_reduce(WS, 4, 8, DW, None, None) == E_NULL
     assert L.layernorm_dwdb_reduce(None, 4, 8, DW, DB, None) == E_NULL

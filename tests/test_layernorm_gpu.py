@@ -61,6 +61,25 @@ def test_small_shapes(dtype, M, N):
     compare_ln_with_oracle(LnRun(w))
 
 
+# Forward shapes the planner gives four or five vectors per lane, at row
+# counts where the forward grid is persistent with two multi-wave row groups
+# per workgroup (the last row step ragged for 8195 and 8200 rows); and
+# backward rows of 5-8 waves run as one workgroup of two or three row groups
+# per CU with the next row's loads in flight.  Each in place and not, with the
+# split and the fused backward.
+LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16", 4100, 6144), ("f32", 3000, 4096),
+         ("f16", 4097, 8192), ("bf16", 4100, 8192), ("f16", 2049, 5120)]
+
+
+@pytest.mark.parametrize("dtype,M,N", LARGE, ids=[f"{d}-{m}x{n}" for d, m, n in LARGE])
+def test_persistent_and_wide_workgroup_shapes(dtype, M, N):
+    w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
+                    dy=wl.LN1.dy, eps=1e-5, seed=M * 11 + N)
+    for split, in_place in ((True, False), (False, True)):
+        _print_case(w.name, "split" if split else "fused", "in place" if in_place else "")
+        compare_ln_with_oracle(LnRun(w, split_bwd=split, in_place=in_place))
+
+
 @pytest.mark.parametrize("N", [1024, 8192, 13312, 15872])
 def test_sweep_points(N):
     """Points of the chapter's bandwidth sweep (M = 4096, fp16) in full."""

@@ -115,6 +115,16 @@ SMALL = [
     ("f32", 150, 704, False, False),    # 2 x 2
     ("f32", 90, 1600, True, True),      # 4 x 2
     ("bf16", 129, 1096, False, False),  # forward one wave of 4
+    # backward rows of 5-8 waves where the partial rows would be a large share
+    # of the traffic: one workgroup of two or three row groups per CU, the
+    # next row's loads in flight (odd numbers of row steps: the loop runs one
+    # step past the last, on rows past M)
+    ("bf16", 2050, 8192, True, True),   # 8 x 2, 5 row steps
+    ("f16", 3001, 6144, False, False),  # 6 x 2
+    ("f32", 2000, 4096, False, True),   # fp32 8 x 2
+    ("bf16", 1500, 5120, True, False),  # 5 x 2, three row groups (15 waves)
+    # persistent forward of 4-wave rows, two row groups per workgroup
+    ("bf16", 8200, 4096, False, True),
 ]
 
 
