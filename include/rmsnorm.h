@@ -29,8 +29,9 @@
  *    RMSNORM_ROUND_NORMED).
  *  - All pointers are device pointers to memory the caller owns (for example
  *    PyTorch tensors).  The library allocates nothing and keeps no state
- *    between calls; calls are asynchronous on `stream` (0 = the null stream)
- *    and their outputs are valid once the stream has reached them.
+ *    between calls (the one exception is rmsnorm_bwd_noalloc's static
+ *    scratch, below); calls are asynchronous on `stream` (0 = the null
+ *    stream) and their outputs are valid once the stream has reached them.
  *  - Arguments are validated on the host before anything is launched.  On any
  *    error nothing is launched and nothing is written.  Status codes are
  *    returned, never thrown.  There is no fallback path of any kind.
@@ -81,7 +82,9 @@ typedef enum {
   RMSNORM_E_WORKSPACE = -8, /* workspace smaller than rmsnorm_bwd_workspace_bytes() (or
                                layernorm_bwd_workspace_bytes() for the LayerNorm backward) */
   RMSNORM_E_FLAG = -9,      /* flags has a bit other than RMSNORM_GEMMA | RMSNORM_ROUND_NORMED */
-  RMSNORM_E_HIP = -10       /* a HIP launch failed */
+  RMSNORM_E_HIP = -10,      /* a HIP launch failed */
+  RMSNORM_E_SCRATCH = -11   /* rmsnorm_bwd_noalloc: the problem needs more partial rows than the
+                               library's static scratch holds (RMSNORM_STATIC_SCRATCH_BYTES) */
 } rmsnorm_status;
 
 /* Largest supported row length (columns), row count, and partials table
@@ -90,6 +93,12 @@ typedef enum {
 #define RMSNORM_N_MAX 16384
 #define RMSNORM_M_MAX (1LL << 29)
 #define RMSNORM_PARTIALS_MAX (1LL << 29)
+
+/* Size of the static device scratch behind rmsnorm_bwd_noalloc (one copy per
+ * GPU the library runs on, held until the process ends).  Every launch plan
+ * of the backward row pass needs at most 17.5 MiB of partial rows (fp32
+ * N = 8960 at 512 partial rows), so every accepted shape fits. */
+#define RMSNORM_STATIC_SCRATCH_BYTES (32LL << 20)
 
 /*
  * Forward: y = x * r * w and the saved r (tutorial, "Vấn đề và công thức tham
@@ -157,6 +166,28 @@ int rmsnorm_dgamma_reduce(const float* partials, int64_t rows, int64_t N, float*
 int rmsnorm_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx, float* dgamma,
                 void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t row_stride, int dtype,
                 int flags, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * full backward as rmsnorm_bwd (same kernels, same launch plan, bitwise the
+ * same dx and dgamma), with the partial rows kept in a static device array
+ * of the library, RMSNORM_STATIC_SCRATCH_BYTES per GPU, instead of a
+ * caller's workspace.  Calls no hipMalloc, hipFree or allocating routine; the
+ * first call on a device resolves that device's copy of the array (a symbol
+ * lookup), later calls reuse it.
+ *
+ * The array is shared by every call on a GPU and holds the last call's
+ * partial rows; the row pass overwrites every row it uses, so nothing needs
+ * clearing.  Calls that overlap on one GPU (concurrent streams, or other
+ * threads) race on it: serialise them.  Arguments and errors as rmsnorm_bwd,
+ * without the workspace; RMSNORM_E_SCRATCH if the launch plan's partial rows
+ * (rows x N x 4 bytes) exceed RMSNORM_STATIC_SCRATCH_BYTES (no shape the
+ * current planner emits does), RMSNORM_E_HIP if the symbol lookup fails.
+ */
+int rmsnorm_bwd_noalloc(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx,
+                        float* dgamma, int64_t M, int64_t N, int64_t row_stride, int dtype, int flags,
+                        hipStream_t stream);
 
 /* A static, human-readable description of a status code. */
 const char* rmsnorm_status_string(int status);

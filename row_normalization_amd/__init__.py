@@ -21,6 +21,7 @@ from ._lib import (
     swiglu_bwd,
     swiglu_fwd,
     rmsnorm_bwd,
+    rmsnorm_bwd_noalloc,
     rmsnorm_bwd_rows,
     rmsnorm_bwd_workspace_bytes,
     rmsnorm_dgamma_reduce,
@@ -37,6 +38,7 @@ __all__ = [
     "lib",
     "rmsnorm_fwd",
     "rmsnorm_bwd",
+    "rmsnorm_bwd_noalloc",
     "rmsnorm_bwd_rows",
     "rmsnorm_dgamma_reduce",
     "rmsnorm_bwd_workspace_bytes",

@@ -27,7 +27,7 @@ GEMMA, ROUND_NORMED = 1, 2  # bits of the C ABI's flags argument
 STATUS = {
     0: "RMSNORM_OK", -1: "RMSNORM_E_NULL", -2: "RMSNORM_E_SHAPE", -3: "RMSNORM_E_STRIDE", -4: "RMSNORM_E_ALIGN",
     -5: "RMSNORM_E_DTYPE", -6: "RMSNORM_E_EPS", -7: "RMSNORM_E_ALIAS", -8: "RMSNORM_E_WORKSPACE",
-    -9: "RMSNORM_E_FLAG", -10: "RMSNORM_E_HIP",
+    -9: "RMSNORM_E_FLAG", -10: "RMSNORM_E_HIP", -11: "RMSNORM_E_SCRATCH",
 }
 
 _c_i64 = ctypes.c_int64
@@ -42,6 +42,8 @@ _SIGNATURES = {
     "rmsnorm_dgamma_reduce": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "rmsnorm_bwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_i64, _c_i64, _c_i64,
                                    ctypes.c_int, ctypes.c_int, _c_p]),
+    "rmsnorm_bwd_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                           ctypes.c_int, _c_p]),
     "rmsnorm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "layernorm_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float,
                                      ctypes.c_int, _c_p]),
@@ -250,6 +252,18 @@ def rmsnorm_bwd(x, gamma, dy, rstd, dx, dgamma, workspace, gemma: bool = False, 
         st = lib().rmsnorm_bwd(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
                                wbytes, M, N, stride, _dtype_code(x), _flags(gemma), _stream(stream, dev))
     _check(st, "rmsnorm_bwd")
+
+
+def rmsnorm_bwd_noalloc(x, gamma, dy, rstd, dx, dgamma, gemma: bool = False, stream=None) -> None:
+    """The full backward with the library's static scratch in place of a
+    workspace (no device allocation; calls on one GPU must not overlap)."""
+    M, N, stride = _bwd_checks(x, gamma, dy, rstd, dx)
+    dev = _gpu(x, dgamma)
+    _vec(dgamma, N, torch.float32, "dgamma")
+    with torch.cuda.device(dev):
+        st = lib().rmsnorm_bwd_noalloc(_ptr(x), _ptr(gamma), _ptr(dy), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N,
+                                       stride, _dtype_code(x), _flags(gemma), _stream(stream, dev))
+    _check(st, "rmsnorm_bwd_noalloc")
 
 
 # ---------------------------------------------------------------------------

@@ -213,4 +213,9 @@ hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t s);
 hipError_t launch_swiglu_fwd(int dtype, int vec, const SwigluArgs& a, hipStream_t s);
 hipError_t launch_swiglu_bwd(int dtype, int vec, const SwigluArgs& a, hipStream_t s);
 
+// The current device's copy of the library's static scratch (the fp32
+// partial rows of rmsnorm_bwd_noalloc, RMSNORM_STATIC_SCRATCH_BYTES per GPU): its
+// device address, looked up once per device.  Returns the lookup's error.
+hipError_t static_scratch(void** ptr);
+
 }  // namespace rmsn

@@ -21,23 +21,25 @@ int check_common(int64_t M, int64_t N, int64_t stride, int dtype, int flags) {
   if (flags & ~(RMSNORM_GEMMA | RMSNORM_ROUND_NORMED)) return RMSNORM_E_FLAG;
   return check_shape(M, N, stride);
 }
-// Validation shared by rmsnorm_bwd_rows and rmsnorm_bwd.  `dgamma` is null
-// for the row pass alone.
+// Validation shared by rmsnorm_bwd_rows, rmsnorm_bwd and rmsnorm_bwd_noalloc.
+// `dgamma` is null for the row pass alone; `own_scratch` skips the checks of
+// the caller's workspace (the no-alloc entry point uses the library's static
+// scratch, which no caller buffer can overlap).
 int check_bwd(const void* x, const void* gamma, const void* dy, const float* rstd, const void* dx, const float* dgamma,
               const void* workspace, size_t workspace_bytes, int64_t M, int64_t N, int64_t stride, int dtype, int flags,
-              bool with_dgamma, int64_t* rows_written) {
+              bool with_dgamma, int64_t* rows_written, bool own_scratch = false) {
   int st = check_common(M, N, stride, dtype, flags);
   if (st) return st;
   if (with_dgamma && !dgamma) return RMSNORM_E_NULL;
   if (with_dgamma && !aligned(dgamma, 4)) return RMSNORM_E_ALIGN;
   *rows_written = 0;
   if (M == 0) return RMSNORM_OK;
-  if (!x || !gamma || !dy || !rstd || !dx || !workspace) return RMSNORM_E_NULL;
+  if (!x || !gamma || !dy || !rstd || !dx || (!workspace && !own_scratch)) return RMSNORM_E_NULL;
   const int es = elsize(dtype);
   if (!aligned(x, es) || !aligned(gamma, es) || !aligned(dy, es) || !aligned(dx, es) || !aligned(rstd, 4) ||
       !aligned(workspace, 4))
     return RMSNORM_E_ALIGN;
-  const int64_t need = partial_rows_bound(M) * N * 4;
+  const int64_t need = own_scratch ? 0 : partial_rows_bound(M) * N * 4;
   if (workspace_bytes < static_cast<size_t>(need)) return RMSNORM_E_WORKSPACE;
   const int64_t mb = matrix_bytes(M, N, stride, dtype);
   const Span sx = span(x, mb), sdy = span(dy, mb), sdx = span(dx, mb), sg = span(gamma, N * es),
@@ -181,6 +183,24 @@ int rmsnorm_bwd(const void* x, const void* gamma, const void* dy, const float* r
   return launch_reduce_checked(static_cast<const float*>(workspace), rows, N, dgamma, stream);
 }
 
+int rmsnorm_bwd_noalloc(const void* x, const void* gamma, const void* dy, const float* rstd, void* dx, float* dgamma,
+                        int64_t M, int64_t N, int64_t row_stride, int dtype, int flags, hipStream_t stream) {
+  int64_t rows = 0;
+  int st = check_bwd(x, gamma, dy, rstd, dx, dgamma, nullptr, 0, M, N, row_stride, dtype, flags, true, &rows, true);
+  if (st) return st;
+  void* scratch = nullptr;
+  if (M > 0) {
+    const RowPlan p = bwd_plan(x, gamma, dy, dx, M, N, row_stride, dtype);
+    if (p.iters == 0) return RMSNORM_E_SHAPE;
+    if (p.grid > RMSNORM_STATIC_SCRATCH_BYTES / (N * 4)) return RMSNORM_E_SCRATCH;
+    st = hip_status(static_scratch(&scratch));
+    if (st) return st;
+    st = launch_bwd_rows_checked(x, gamma, dy, rstd, dx, scratch, M, N, row_stride, dtype, flags, &rows, stream);
+    if (st) return st;
+  }
+  return launch_reduce_checked(static_cast<const float*>(scratch), rows, N, dgamma, stream);
+}
+
 const char* rmsnorm_status_string(int status) {
   switch (status) {
     case RMSNORM_OK: return "ok";
@@ -194,6 +214,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_E_WORKSPACE: return "workspace smaller than the matching *_bwd_workspace_bytes() size";
     case RMSNORM_E_FLAG: return "flags may only combine RMSNORM_GEMMA and RMSNORM_ROUND_NORMED";
     case RMSNORM_E_HIP: return "HIP kernel launch failed";
+    case RMSNORM_E_SCRATCH:
+      return "the launch plan needs more partial rows than the static scratch holds (RMSNORM_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -41,10 +41,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "rmsnorm.h"
 
 namespace rmsn {
 namespace {
@@ -460,6 +462,38 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
     }
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of rmsnorm_bwd_noalloc: the fp32 partial rows of the weight
+// gradient, for callers that cannot allocate.  Every GPU the library runs on
+// holds its own copy until the process ends.  On the host the name is only a
+// stand-in for the symbol (passing it to a kernel would hand the kernel a
+// host address): host code uses the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[RMSNORM_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t s) {

@@ -62,6 +62,14 @@ void check_row_plan(const rmsn::RowPlan& p, rmsn::RowOp op, int dtype, int64_t M
 }  // namespace
 
 namespace rmsn {
+// The static scratch of rmsnorm_bwd_noalloc, stood in for by a fake address.
+char* const kScratch = reinterpret_cast<char*>(uintptr_t(1) << 45);
+long g_scratch_lookups = 0;
+hipError_t static_scratch(void** ptr) {
+  ++g_scratch_lookups;
+  *ptr = kScratch;
+  return hipSuccess;
+}
 hipError_t launch_fwd(int dtype, const RowPlan& p, const FwdArgs& a, hipStream_t) {
   ++g_launches;
   check_row_plan(p, RowOp::kRmsFwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
@@ -75,6 +83,9 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
   expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kRmsBwd, dtype, p.vec, p.iters) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
          "pipelined only where it fits and one workgroup fills the CU");
   expect(p.grid <= partial_rows_bound(a.M), "partial rows within the workspace", p.grid);
+  expect(reinterpret_cast<const char*>(a.partials) != kScratch ||
+             p.grid * int64_t(a.N) * 4 <= RMSNORM_STATIC_SCRATCH_BYTES,
+         "partial rows within the static scratch", p.grid, a.N);
   return hipSuccess;
 }
 hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t) {
@@ -169,6 +180,9 @@ void norms(int64_t M, int64_t N, int64_t stride, int dtype, int64_t mis) {
                             reinterpret_cast<float*>(slot(7)), slot(6), wbytes, M, N, stride, dtype,
                             flags & RMSNORM_GEMMA, s),
                 "rmsnorm_bwd", M, N);
+      expect_ok(rmsnorm_bwd_noalloc(slot(0, off), slot(1), dy, reinterpret_cast<const float*>(slot(3)), dx,
+                                    reinterpret_cast<float*>(slot(7)), M, N, stride, dtype, flags & RMSNORM_GEMMA, s),
+                "rmsnorm_bwd_noalloc", M, N);
     }
   }
   expect_ok(layernorm_fwd(slot(0, off), slot(1), slot(8), slot(2, off), reinterpret_cast<float*>(slot(3)),
@@ -259,6 +273,7 @@ int main() {
     }
   expect(g_launches == launches_before, "no launch for a rejected table");
 
+  expect(rmsn::g_scratch_lookups > 0, "the static scratch was used");
   std::printf("%ld launches checked, %ld checks, %ld bad\n", g_launches, g_checks, g_bad);
   return g_bad ? 1 : 0;
 }

@@ -38,7 +38,7 @@ def L():
 def test_library_exports_every_declared_symbol(L):
     names = rn.header_functions()
     assert set(names) == {"rmsnorm_fwd", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd_rows", "rmsnorm_dgamma_reduce",
-                          "rmsnorm_bwd", "rmsnorm_status_string", "layernorm_fwd", "layernorm_bwd_workspace_bytes",
+                          "rmsnorm_bwd", "rmsnorm_bwd_noalloc", "rmsnorm_status_string", "layernorm_fwd", "layernorm_bwd_workspace_bytes",
                           "layernorm_bwd_rows", "layernorm_dwdb_reduce", "layernorm_bwd", "rope_fwd", "rope_bwd",
                           "swiglu_fwd", "swiglu_bwd"}
     for n in names:
@@ -59,7 +59,7 @@ def test_library_has_gfx950_code_only():
 
 
 def test_status_strings(L):
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         assert rn.rmsnorm_status_string(code) not in ("", "unknown status")
     assert rn.rmsnorm_status_string(-99) == "unknown status"
 
@@ -158,6 +158,32 @@ def test_bwd_specific_rejections(L):
     out = ctypes.c_int64(-5)
     assert L.rmsnorm_bwd_rows(None, None, None, None, None, None, 0, 0, 8, 8, BF16, 0, ctypes.byref(out), None) == OK
     assert out.value == 0
+
+
+def noalloc(L, x=X, g=G, dy=DY, r=R, dx=DX, dg=DG, M=4, N=8, stride=None, dtype=BF16, gemma=0):
+    return L.rmsnorm_bwd_noalloc(x, g, dy, r, dx, dg, M, N, N if stride is None else stride, dtype, gemma, None)
+
+
+def test_bwd_noalloc_rejections(L):
+    # the same validation as rmsnorm_bwd, before anything touches the GPU
+    # (the static scratch is not even looked up on an invalid call)
+    assert noalloc(L, dtype=3) == E_DTYPE
+    assert noalloc(L, gemma=8) == E_FLAG
+    assert noalloc(L, N=0) == E_SHAPE
+    assert noalloc(L, N=16385) == E_SHAPE
+    assert noalloc(L, M=-1) == E_SHAPE
+    assert noalloc(L, M=(1 << 29) + 1) == E_SHAPE
+    assert noalloc(L, stride=7) == E_STRIDE
+    for kw in ("x", "g", "dy", "r", "dx", "dg"):
+        assert noalloc(L, **{kw: None}) == E_NULL, kw
+    assert noalloc(L, dy=DY + 1) == E_ALIGN
+    assert noalloc(L, dg=DG + 2) == E_ALIGN
+    assert noalloc(L, dx=X) == E_ALIAS
+    assert noalloc(L, dx=DY + 2) == E_ALIAS
+    assert noalloc(L, dg=DX) == E_ALIAS
+    assert noalloc(L, g=DX + 4) == E_ALIAS
+    assert noalloc(L, M=0, x=None, g=None, dy=None, r=None, dx=None, dg=None) == E_NULL  # dgamma still required
+    assert rn.rmsnorm_status_string(-11).startswith("the launch plan needs more partial rows")
 
 
 def test_dgamma_reduce_rejections(L):
