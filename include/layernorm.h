@@ -38,6 +38,12 @@
 
 #include "rmsnorm.h"
 
+/* Longest LayerNorm row: the chapter's forward wrapper takes rows of up to
+ * 64 KB (Step 2, the wrapper's block-size limit).  bf16 and fp16 rows may have up
+ * to 32768 elements (rows beyond 16384 run in chunked kernels, one 1024-thread
+ * workgroup per row); fp32 rows, as for RMSNorm, up to RMSNORM_N_MAX = 16384. */
+#define LAYERNORM_N_MAX_16BIT 32768
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -88,7 +94,7 @@ int layernorm_bwd_rows(const void* x, const void* weight, const void* dy, const 
  *
  *   partials  [2 * rows, N] fp32, contiguous, read (may be NULL when rows == 0)
  *   dw, db    [N] fp32, overwritten (zeros when rows == 0)
- * Errors: RMSNORM_E_SHAPE when rows < 0, N outside [1, RMSNORM_N_MAX] or
+ * Errors: RMSNORM_E_SHAPE when rows < 0, N outside [1, LAYERNORM_N_MAX_16BIT] or
  * 2 * rows * N > RMSNORM_PARTIALS_MAX; RMSNORM_E_ALIAS when an output overlaps
  * the partials or the other output.
  */

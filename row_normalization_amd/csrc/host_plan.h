@@ -80,9 +80,10 @@ inline int64_t matrix_bytes(int64_t M, int64_t N, int64_t stride, int dtype) {
   return M == 0 ? 0 : ((M - 1) * stride + N) * elsize(dtype);
 }
 
-// Shape and stride limits shared by every row operation.
-inline int check_shape(int64_t M, int64_t N, int64_t stride) {
-  if (M < 0 || M > RMSNORM_M_MAX || N < 1 || N > RMSNORM_N_MAX) return RMSNORM_E_SHAPE;
+// Shape and stride limits shared by every row operation (n_max: the longest
+// row the operation takes).
+inline int check_shape(int64_t M, int64_t N, int64_t stride, int64_t n_max = RMSNORM_N_MAX) {
+  if (M < 0 || M > RMSNORM_M_MAX || N < 1 || N > n_max) return RMSNORM_E_SHAPE;
   if (stride < N) return RMSNORM_E_STRIDE;
   // element offsets must stay well inside int64 even for the last row
   if (M > 0 && stride > (std::numeric_limits<int64_t>::max() / 8) / M) return RMSNORM_E_SHAPE;
@@ -142,24 +143,36 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
   return found;
 }
 
-// Whether a backward whose rows span 5-8 waves (one row per workgroup of the
-// kBlockWaves-wave shape, two such workgroups per CU) should run one
-// workgroup of two row groups per CU instead: half the partial rows.  Each
-// workgroup writes one fp32 partial row per weight (two for LayerNorm),
-// which the column sum reads back; with `grid` workgroups of the smaller
-// shape that is tables * grid * 4 bytes per column against 3 * M * es of row
-// traffic.  The wide workgroups are taken where that share exceeds
-// kBwdWideShare and the pipelined row loop is compiled for the plan (a single
-// workgroup per CU needs it to keep loads in flight through its barriers).
-// Measured on MI355X (row pass, interleaved comparison): LayerNorm fp16
-// 4096 x 6144 (share 0.17) 10 %, 4096 x 8192 (0.17) 3 %, 16384 x 8192 (0.042)
-// 2 %, fp32 4096 x 4096 (0.083) 3 % and RMSNorm bf16 2048 x 8192 (0.17) 4 %
-// faster; RMSNorm bf16 16384 x 8192 (0.021) 2.3 % and 32768 x 5120 (0.010)
-// 3.7 % slower.  Rows of fewer waves were 3-37 % slower in wide workgroups
-// (4-16 row groups to combine per workgroup), so they keep the smaller shape.
+// Backward grids where the weight-gradient partial rows are a heavy share of
+// the traffic.  Each backward workgroup writes one fp32 partial row per
+// weight (two for LayerNorm) after its last row step, which the column sum
+// reads back: with `grid` workgroups, tables * grid * 4 bytes per column
+// against 3 * M * es of row traffic.  Where that share exceeds kBwdWideShare
+// (and the pipelined row loop is compiled for the plan: a workgroup alone on
+// its CU needs it to keep loads in flight through its barriers), the
+// backward runs one workgroup per CU instead of two:
+//   * rows of 5-8 waves as workgroups of two row groups (16 waves);
+//   * other rows keep their workgroup shape, one per CU;
+//   * each workgroup takes at least kBwdMinSteps row steps while the grid
+//     keeps kBwdMinGridWaves waves (8 per CU), and the grid is then the
+//     fewest workgroups that keep the step count and those waves.
+// Measured on MI355X (interleaved comparison; full backward = row pass and
+// column sum): LayerNorm fp16 at M = 4096, N = 1024-5120, 4-17 % faster
+// (N = 1024 17 %, 2048 15 %, 4096 16 %), the chapter's 1151 x 8192 17 %,
+// 8192 x 2048 12 %, fp32 4096 x 2048 10 %; RMSNorm bf16 4096 x 4096 10 %,
+// 4096 x 3072 13 %, 8192 x 2048 6.5 %, 1151 x 8192 9 %, 700 x 16384 7 %.
+// Shapes below the share (16384 x 8192, 32768 x 5120, 16384 x 1024) are
+// unchanged: there two workgroups of the row shape per CU were faster (the
+// 16-wave shape 2-4 % slower at 16384 x 8192 and 32768 x 5120).  Rows of 1-4
+// waves in 16-wave workgroups (4-16 row groups to combine) were 3-37 %
+// slower, so they keep their shape; one workgroup per CU of fewer than
+// kBwdMinGridWaves / 256 waves was slower (4096 x 1024 with 128 workgroups
+// of 8 waves: 13 %).
 constexpr double kBwdWideShare = 0.03;
-inline bool bwd_wide_workgroups(RowOp op, int64_t M, int es, int wpr, int64_t grid) {
-  if (wpr * 2 <= kBlockWaves || wpr > kBlockWaves) return false;
+constexpr int64_t kBwdMinSteps = 4;
+constexpr int64_t kBwdMinGridWaves = 2048;
+
+inline bool bwd_partials_heavy(RowOp op, int64_t M, int es, int64_t grid) {
   const int tables = op == RowOp::kLnBwd ? 2 : 1;
   return static_cast<double>(tables) * static_cast<double>(grid) * 4.0 >
          kBwdWideShare * 3.0 * static_cast<double>(M) * es;
@@ -247,9 +260,11 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
   int64_t per_cu = 1;
   while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
   if (backward && bwd_pipeline_fits(op, dtype, p.vec, p.iters) &&
-      bwd_wide_workgroups(op, M, es, p.wpr, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)))) {
-    p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
-    groups = ceil_div(M, p.rpb);
+      bwd_partials_heavy(op, M, es, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)))) {
+    if (p.wpr * 2 > kBlockWaves && p.wpr <= kBlockWaves) {  // rows of 5-8 waves: two per workgroup
+      p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
+      groups = ceil_div(M, p.rpb);
+    }
     per_cu = 1;
   }
   // The forward is persistent where that grid fills every CU with
@@ -279,20 +294,43 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
                            : fwd_persistent ? kComputeUnits * per_cu
                                             : kFwdGridMax;
   p.grid = std::max<int64_t>(1, std::min(groups, grid_cap));
+  const bool one_per_cu = backward && p.grid <= kComputeUnits;
+  const int64_t floor_grid = ceil_div(kBwdMinGridWaves, static_cast<int64_t>(p.wpr) * p.rpb);
+  if (one_per_cu) p.grid = std::max<int64_t>(1, std::min(p.grid, std::max(ceil_div(groups, kBwdMinSteps), floor_grid)));
   p.row_iters = ceil_div(groups, p.grid);
+  if (one_per_cu) p.grid = std::max<int64_t>(1, std::min(p.grid, std::max(ceil_div(groups, p.row_iters), floor_grid)));
   return p;
 }
 
 inline int64_t partial_rows_bound(int64_t M) { return std::min(M, kBwdGridMax); }
 
+// Plan of the wide LayerNorm kernels, for 16-bit rows beyond RMSNORM_N_MAX
+// (up to kLnWideMaxN elements): one 1024-thread workgroup per
+// row, iters = chunks of 1024 vectors per row; the backward is persistent,
+// one workgroup per CU (each writes one dw and one db partial row), the
+// forward takes a row per workgroup.
+inline RowPlan plan_ln_wide(bool backward, int64_t M, int64_t N, int vec) {
+  RowPlan p{};
+  p.vec = vec;
+  p.wpr = kMaxBlockWaves;
+  p.rpb = 1;
+  p.iters = static_cast<int>(ceil_div(N / vec, int64_t(kMaxBlockWaves) * kWave));
+  p.grid = std::max<int64_t>(1, std::min(M, backward ? kComputeUnits : kFwdGridMax));
+  p.row_iters = ceil_div(M, p.grid);
+  return p;
+}
+
 // Whether a backward workgroup should keep the next row's loads in flight
-// while it works on a row: only where one workgroup fills its CU's resident
-// waves, so no other workgroup's loads cover the row's reduction and barrier.
-// Measured on MI355X (bf16): 8192 x 16384, 8192 x 15872, 16384 x 15360 and
-// 16384 x 9216 row passes 5-9 % faster pipelined; with two workgroups per CU
-// (16384 x 8192, 32768 x 5120) pipelining was 2-8 % slower.
+// while it works on a row: only where it is alone on its CU (it fills the
+// CU's resident waves, or the grid has one workgroup per CU), so no other
+// workgroup's loads cover the row's reduction and barrier.  Measured on
+// MI355X (bf16): 8192 x 16384, 8192 x 15872, 16384 x 15360 and 16384 x 9216
+// row passes 5-9 % faster pipelined; one 8-wave workgroup per CU at LayerNorm
+// fp16 4096 x 2048 16 % faster pipelined than not; with two workgroups per
+// CU (16384 x 8192, 32768 x 5120) pipelining was 2-8 % slower.
 inline bool bwd_pipelined(RowOp op, const RowPlan& p, int dtype) {
-  return p.wpr * p.rpb * 2 > kBwdResidentWaves && bwd_pipeline_fits(op, dtype, p.vec, p.iters);
+  const bool alone_on_cu = p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits;
+  return alone_on_cu && bwd_pipeline_fits(op, dtype, p.vec, p.iters);
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_E_HIP; }

@@ -94,6 +94,7 @@ struct LnFwdArgs {
   int32_t wpr;
   int32_t rpb;
   int64_t row_iters;
+  int32_t chunks;  // wide rows only: 1024-vector chunks per row
 };
 
 // LayerNorm backward row pass: dx, and per-workgroup partial rows of dw
@@ -115,7 +116,15 @@ struct LnBwdArgs {
   int32_t rpb;
   int64_t row_iters;
   int32_t pipeline;  // as in BwdArgs
+  int32_t chunks;    // wide rows only: 1024-vector chunks per row
 };
+
+// LayerNorm rows of 16-bit elements beyond the register plans (up to
+// kLnWideMaxN elements, 64 KB) run in the wide kernels: one 1024-thread
+// workgroup per row, lane t owning vector k * 1024 + t of each 1024-vector
+// chunk k, so at most kLnWideColsPerLane columns per lane.
+constexpr int kLnWideMaxN = 32768;
+constexpr int kLnWideColsPerLane = kLnWideMaxN / 1024;
 
 // RoPE: one work item = one token, one group of kRopeGroup heads, one VEC
 // vector of the half-head (and the matching vector of the other half).
@@ -209,6 +218,10 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
 hipError_t launch_dgamma_reduce(int vec, int tables, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_ln_fwd(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s);
 hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t s);
+// Wide LayerNorm rows (16-bit dtypes only): p.vec, p.grid, p.row_iters and
+// a.chunks from plan_ln_wide.
+hipError_t launch_ln_fwd_wide(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s);
+hipError_t launch_ln_bwd_wide(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t s);
 hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t s);
 hipError_t launch_swiglu_fwd(int dtype, int vec, const SwigluArgs& a, hipStream_t s);
 hipError_t launch_swiglu_bwd(int dtype, int vec, const SwigluArgs& a, hipStream_t s);

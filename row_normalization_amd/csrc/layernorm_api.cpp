@@ -15,7 +15,7 @@ namespace {
 
 int check_dtype_shape(int64_t M, int64_t N, int64_t stride, int dtype) {
   if (dtype != RMSNORM_F32 && dtype != RMSNORM_BF16 && dtype != RMSNORM_F16) return RMSNORM_E_DTYPE;
-  return check_shape(M, N, stride);
+  return check_shape(M, N, stride, dtype == RMSNORM_F32 ? RMSNORM_N_MAX : LAYERNORM_N_MAX_16BIT);
 }
 
 // Two partial tables (dw, db) of up to partial_rows_bound(M) rows each.
@@ -57,7 +57,8 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
                                const float* rstd, void* dx, void* workspace, int64_t M, int64_t N, int64_t stride,
                                int dtype, int64_t* rows_written, hipStream_t stream) {
   const int vec = choose_vec(dtype, N, stride, {x, weight, dy, dx});
-  const RowPlan p = plan_rows(RowOp::kLnBwd, M, N, vec, dtype);
+  const bool wide = N > RMSNORM_N_MAX;  // 16-bit rows only (check_dtype_shape)
+  const RowPlan p = wide ? plan_ln_wide(true, M, N, vec) : plan_rows(RowOp::kLnBwd, M, N, vec, dtype);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnBwdArgs a{};
   a.x = x;
@@ -75,8 +76,9 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
-  a.pipeline = bwd_pipelined(RowOp::kLnBwd, p, dtype);
-  const int st = hip_status(launch_ln_bwd_rows(dtype, p, a, stream));
+  a.pipeline = wide ? 0 : bwd_pipelined(RowOp::kLnBwd, p, dtype);
+  a.chunks = wide ? p.iters : 0;
+  const int st = hip_status(wide ? launch_ln_bwd_wide(dtype, p, a, stream) : launch_ln_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;
   return st;
 }
@@ -115,7 +117,8 @@ int layernorm_fwd(const void* x, const void* weight, const void* bias, void* y, 
   if (overlap(sy, sm) || overlap(sy, sr) || overlap(sm, sr)) return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, weight, bias, y});
-  const RowPlan p = plan_rows(RowOp::kLnFwd, M, N, vec, dtype);
+  const bool wide = N > RMSNORM_N_MAX;  // 16-bit rows only (check_dtype_shape)
+  const RowPlan p = wide ? plan_ln_wide(false, M, N, vec) : plan_rows(RowOp::kLnFwd, M, N, vec, dtype);
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnFwdArgs a{};
   a.x = x;
@@ -133,7 +136,8 @@ int layernorm_fwd(const void* x, const void* weight, const void* bias, void* y, 
   a.wpr = p.wpr;
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
-  return hip_status(launch_ln_fwd(dtype, p, a, stream));
+  a.chunks = wide ? p.iters : 0;
+  return hip_status(wide ? launch_ln_fwd_wide(dtype, p, a, stream) : launch_ln_fwd(dtype, p, a, stream));
 }
 
 int layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t* bytes) {
@@ -159,7 +163,7 @@ int layernorm_bwd_rows(const void* x, const void* weight, const void* dy, const 
 
 int layernorm_dwdb_reduce(const float* partials, int64_t rows, int64_t N, float* dw, float* db, hipStream_t stream) {
   // two tables of rows x N; bounded by division, as 2 * rows * N could wrap
-  if (rows < 0 || N < 1 || N > RMSNORM_N_MAX || rows > RMSNORM_PARTIALS_MAX / (2 * N)) return RMSNORM_E_SHAPE;
+  if (rows < 0 || N < 1 || N > LAYERNORM_N_MAX_16BIT || rows > RMSNORM_PARTIALS_MAX / (2 * N)) return RMSNORM_E_SHAPE;
   if (!dw || !db || (rows > 0 && !partials)) return RMSNORM_E_NULL;
   if (!aligned(dw, 4) || !aligned(db, 4) || (rows > 0 && !aligned(partials, 4))) return RMSNORM_E_ALIGN;
   const Span sp = span(partials, 2 * rows * N * 4), sw = span(dw, N * 4), sb = span(db, N * 4);

@@ -360,13 +360,13 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
       for (int i = 0; i < ITERS; ++i) {
         const int v = (i * a.wpr + L.wv) * kWave + L.lane;
         if (v < a.nvec) {
-          float* cw = comb + v * VEC;
-          float* cb = comb + a.N + v * VEC;
+          float* cw = comb;
+          float* cb = comb + a.N;
           if (g == 0) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-              cw[e] = accw[i][e];
-              cb[e] = accb[i][e];
+              cw[comb_index<VEC>(v, e, a.nvec)] = accw[i][e];
+              cb[comb_index<VEC>(v, e, a.nvec)] = accb[i][e];
             }
           } else {
             // Both tables' cells are read before either is written: the
@@ -377,13 +377,13 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
             float tw[VEC], tb[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-              tw[e] = cw[e];
-              tb[e] = cb[e];
+              tw[e] = cw[comb_index<VEC>(v, e, a.nvec)];
+              tb[e] = cb[comb_index<VEC>(v, e, a.nvec)];
             }
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-              cw[e] = tw[e] + accw[i][e];
-              cb[e] = tb[e] + accb[i][e];
+              cw[comb_index<VEC>(v, e, a.nvec)] = tw[e] + accw[i][e];
+              cb[comb_index<VEC>(v, e, a.nvec)] = tb[e] + accb[i][e];
             }
           }
         }
@@ -397,12 +397,12 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
     for (int i = 0; i < ITERS; ++i) {
       const int v = (i * a.wpr + L.wv) * kWave + L.lane;
       if (v < a.nvec) {
-        const float* cw = comb + v * VEC;
-        const float* cb = comb + a.N + v * VEC;
+        const float* cw = comb;
+        const float* cb = comb + a.N;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          accw[i][e] += cw[e];
-          accb[i][e] += cb[e];
+          accw[i][e] += cw[comb_index<VEC>(v, e, a.nvec)];
+          accb[i][e] += cb[comb_index<VEC>(v, e, a.nvec)];
         }
       }
     }
@@ -415,6 +415,195 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
   for (int i = 0; i < ITERS; ++i) {
     buf_store_f32<VEC, kDefault>(accw[i], rdw, voff32 + i * iter32);
     buf_store_f32<VEC, kDefault>(accb[i], rdb, voff32 + i * iter32);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide rows: 16-bit rows beyond the register plans (up to kLnWideMaxN
+// elements, the 64 KB per row of the chapter's Step 2 wrapper), one 1024-thread
+// workgroup per row.  Lane t owns vector k * 1024 + t of the row for each
+// chunk k < chunks (at most kLnWideColsPerLane columns per lane); vectors at
+// or past N / VEC read zero and store nothing through the row descriptors.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 1024;
+
+// Sums of one value per lane over the workgroup's 16 waves (as group_sum2,
+// slots alternating with the step parity).
+__device__ __forceinline__ void block_sum2(float& s1, float& s2, float (*red)[2][kMaxBlockWaves], int64_t step,
+                                           const Lane& L) {
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  group_sum2(s1, s2, red, step, L.wave, 0, kWideThreads / kWave, L.lane);
+}
+
+// Forward over a row held in registers (x loaded once per row); weight and
+// bias are read per row from the caches (N elements shared by every row).
+template <typename S, int VEC>
+__global__ __launch_bounds__(kWideThreads) void layernorm_fwd_wide_kernel(const LnFwdArgs a) {
+  constexpr int KMAX = kLnWideColsPerLane / VEC;
+  constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  const Lane L(kWideThreads / kWave);
+  __shared__ float red[2][2][kMaxBlockWaves];
+  const int chunks = a.chunks;
+  const int64_t steps = a.row_iters;
+  const uint32_t voff = threadIdx.x * kPack;
+  constexpr uint32_t kChunkBytes = kWideThreads * kPack;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  const Rsrc rw = make_rsrc(a.weight, row_bytes);
+  const Rsrc rb = make_rsrc(a.bias, row_bytes);
+  const Rsrc rmean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
+  const Rsrc rrstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+  for (int64_t step = 0; step < steps; ++step) {
+    const int64_t row = step * gridDim.x + blockIdx.x;
+    const bool active = row < a.M;
+    const int64_t off = active ? row * a.stride : 0;
+    const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? row_bytes : 0u);
+    const Rsrc ry = make_rsrc(static_cast<S*>(a.y) + off, active ? row_bytes : 0u);
+    Pack<S, VEC> xv[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      xv[k] = buf_load<S, VEC, kLnLoadX>(rx, k < chunks ? voff + k * kChunkBytes : kOutOfRange);
+    float s = 0.f, unused = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s += xv[k].get(e);
+    block_sum2(s, unused, red, 2 * step, L);
+    const float mean = s * a.inv_n;
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const bool in_row = static_cast<int>(k * kWideThreads + threadIdx.x) < a.nvec;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float t = in_row ? xv[k].get(e) - mean : 0.f;
+        d = fmaf(t, t, d);
+      }
+    }
+    block_sum2(d, unused, red, 2 * step + 1, L);
+    const float rstd = rsqrtf(fmaf(d, a.inv_n, a.eps));
+    const uint32_t soff = active && threadIdx.x == 0 ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mean), rmean, soff, 0, kDefault);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, rstd), rrstd, soff, 0, kDefault);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const uint32_t o = k < chunks ? voff + k * kChunkBytes : kOutOfRange;
+      const Pack<S, VEC> wv = buf_load<S, VEC, kDefault>(rw, o);
+      const Pack<S, VEC> bv = buf_load<S, VEC, kDefault>(rb, o);
+      float out[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) out[e] = fmaf((xv[k].get(e) - mean) * rstd, wv.get(e), bv.get(e));
+      buf_store<S, VEC, kLnStoreY>(round_pack<S, VEC>(out), ry, o);
+    }
+  }
+}
+
+// Backward: per row, the two row sums (pass 1), then dx and the dw / db
+// contributions (pass 2).  x and dy stay in registers between the passes for
+// 16-byte vectors; narrower vectors (N not a multiple of 8, or misaligned
+// rows) would need more registers than a lane of a 1024-thread workgroup
+// has, so pass 2 reads them again, from L2 (pass 1 loads them with the
+// allocating policy).  The weight is read per pass from the
+// caches.  dw and db partials stay in fp32 registers across the workgroup's
+// rows; the workgroup writes one partial row of each.
+template <typename S, int VEC>
+__global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_kernel(const LnBwdArgs a) {
+  constexpr int KMAX = kLnWideColsPerLane / VEC;
+  constexpr bool kHold = VEC * sizeof(S) == 16;
+  constexpr int kPass1 = kHold ? kLnLoadXdy : kDefault;
+  constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  const Lane L(kWideThreads / kWave);
+  __shared__ float red[2][2][kMaxBlockWaves];
+  const int chunks = a.chunks;
+  const int64_t steps = a.row_iters;
+  const uint32_t voff = threadIdx.x * kPack;
+  constexpr uint32_t kChunkBytes = kWideThreads * kPack;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  const Rsrc rw = make_rsrc(a.weight, row_bytes);
+  const Rsrc rmean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
+  const Rsrc rrstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+  float accw[KMAX][VEC], accb[KMAX][VEC];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) accw[k][e] = accb[k][e] = 0.f;
+
+  for (int64_t step = 0; step < steps; ++step) {
+    const int64_t row = step * gridDim.x + blockIdx.x;
+    const bool active = row < a.M;
+    const int64_t off = active ? row * a.stride : 0;
+    const Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + off, active ? row_bytes : 0u);
+    const Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + off, active ? row_bytes : 0u);
+    const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + off, active ? row_bytes : 0u);
+    const uint32_t soff = active ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+    const float mean = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rmean, soff, 0, kDefault));
+    const float rstd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrstd, soff, 0, kDefault));
+
+    Pack<S, VEC> xv[kHold ? KMAX : 1], dv[kHold ? KMAX : 1];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const uint32_t o = k < chunks ? voff + k * kChunkBytes : kOutOfRange;
+      const Pack<S, VEC> x = buf_load<S, VEC, kPass1>(rx, o);
+      const Pack<S, VEC> dy = buf_load<S, VEC, kPass1>(rd, o);
+      const Pack<S, VEC> w = buf_load<S, VEC, kDefault>(rw, o);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float xh = (x.get(e) - mean) * rstd;
+        const float g = w.get(e) * dy.get(e);
+        s1 = fmaf(xh, g, s1);
+        s2 += g;
+      }
+      if constexpr (kHold) {
+        xv[k] = x;
+        dv[k] = dy;
+      }
+    }
+    if constexpr (kHold) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        xv[k].keep_packed();
+        dv[k].keep_packed();
+      }
+    }
+    block_sum2(s1, s2, red, step, L);
+    const float c1 = s1 * a.inv_n;
+    const float c2 = s2 * a.inv_n;
+
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const uint32_t o = k < chunks ? voff + k * kChunkBytes : kOutOfRange;
+      Pack<S, VEC> x, dy;
+      if constexpr (kHold) {
+        x = xv[k];
+        dy = dv[k];
+      } else {
+        // every element of dy this lane reads here it has not yet overwritten
+        // (dx may be dy itself: this lane stores only the elements it loads)
+        x = buf_load<S, VEC, kLnLoadXdy>(rx, o);
+        dy = buf_load<S, VEC, kLnLoadXdy>(rd, o);
+      }
+      const Pack<S, VEC> w = buf_load<S, VEC, kDefault>(rw, o);
+      float out[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float df = dy.get(e);
+        const float xh = (x.get(e) - mean) * rstd;
+        out[e] = (w.get(e) * df - fmaf(xh, c1, c2)) * rstd;
+        accw[k][e] = fmaf(df, xh, accw[k][e]);
+        accb[k][e] += df;
+      }
+      buf_store<S, VEC, kLnStoreDx>(round_pack<S, VEC>(out), rdx, o);
+    }
+  }
+  const Rsrc rpw = make_rsrc(a.partials + static_cast<int64_t>(blockIdx.x) * a.N, static_cast<uint32_t>(a.N) * 4u);
+  const Rsrc rpb =
+      make_rsrc(a.partials + (static_cast<int64_t>(gridDim.x) + blockIdx.x) * a.N, static_cast<uint32_t>(a.N) * 4u);
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const uint32_t o = k < chunks ? (k * kWideThreads + threadIdx.x) * VEC * 4u : kOutOfRange;
+    buf_store_f32<VEC, kDefault>(accw[k], rpw, o);
+    buf_store_f32<VEC, kDefault>(accb[k], rpb, o);
   }
 }
 
@@ -456,7 +645,45 @@ hipError_t ln_bwd_vec(const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
                     ln_bwd_inst<S, VEC, 5>, ln_bwd_inst<S, VEC, 8>, ln_bwd_inst<S, VEC, 16>>(p, a, s);
 }
 
+template <typename S>
+hipError_t ln_wide_fwd_s(const RowPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p.grid)), block(kWideThreads);
+  switch (p.vec) {
+    case 1: hipLaunchKernelGGL((layernorm_fwd_wide_kernel<S, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((layernorm_fwd_wide_kernel<S, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((layernorm_fwd_wide_kernel<S, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((layernorm_fwd_wide_kernel<S, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t ln_wide_bwd_s(const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p.grid)), block(kWideThreads);
+  switch (p.vec) {
+    case 1: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_ln_fwd_wide(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  if (dtype == 1) return ln_wide_fwd_s<uint16_t>(p, a, s);
+  if (dtype == 2) return ln_wide_fwd_s<_Float16>(p, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ln_bwd_wide(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
+  if (dtype == 1) return ln_wide_bwd_s<uint16_t>(p, a, s);
+  if (dtype == 2) return ln_wide_bwd_s<_Float16>(p, a, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_ln_fwd(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t s) {
   if (dtype == 0) {

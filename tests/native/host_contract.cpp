@@ -80,8 +80,9 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
   ++g_launches;
   check_row_plan(p, RowOp::kRmsBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 4 <= 65536, "LDS combine size", a.N);
-  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kRmsBwd, dtype, p.vec, p.iters) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
-         "pipelined only where it fits and one workgroup fills the CU");
+  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kRmsBwd, dtype, p.vec, p.iters) &&
+                         (p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits)),
+         "pipelined only where it fits and the workgroup is alone on its CU");
   expect(p.grid <= partial_rows_bound(a.M), "partial rows within the workspace", p.grid);
   expect(reinterpret_cast<const char*>(a.partials) != kScratch ||
              p.grid * int64_t(a.N) * 4 <= RMSNORM_STATIC_SCRATCH_BYTES,
@@ -106,8 +107,38 @@ hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, h
   ++g_launches;
   check_row_plan(p, RowOp::kLnBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 8 <= 65536, "LDS combine size", a.N);
-  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kLnBwd, dtype, p.vec, p.iters) && p.wpr * p.rpb * 2 > kBwdResidentWaves),
-         "pipelined only where it fits and one workgroup fills the CU");
+  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kLnBwd, dtype, p.vec, p.iters) &&
+                         (p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits)),
+         "pipelined only where it fits and the workgroup is alone on its CU");
+  return hipSuccess;
+}
+// What every wide LayerNorm launch must satisfy (16-bit rows beyond the
+// register plans, one 1024-thread workgroup per row).
+static void check_wide_plan(const RowPlan& p, bool bwd, int dtype, int64_t M, int64_t stride, int32_t N, int32_t nvec,
+                            int32_t chunks, int64_t row_iters) {
+  expect(dtype == 1 || dtype == 2, "wide rows are 16-bit", dtype);
+  expect(N > RMSNORM_N_MAX && N <= kLnWideMaxN, "wide rows only beyond the register plans", N);
+  expect(p.vec == 1 || p.vec == 2 || p.vec == 4 || p.vec == 8, "wide vector width", p.vec);
+  expect(N % p.vec == 0 && stride % p.vec == 0 && int64_t(nvec) * p.vec == N, "wide width divides N", N, stride);
+  expect(p.wpr * kWave == 1024 && p.rpb == 1, "wide workgroup", p.wpr, p.rpb);
+  expect(chunks == p.iters && int64_t(chunks) * 1024 >= nvec, "wide row covered", chunks, nvec);
+  expect(chunks * p.vec <= kLnWideColsPerLane, "wide columns per lane", chunks, p.vec);
+  expect(p.grid >= 1 && p.grid * row_iters >= M && row_iters == p.row_iters, "wide rows covered", M);
+  expect(!bwd || p.grid <= partial_rows_bound(M), "wide partial rows within the workspace", p.grid);
+  expect(int64_t(N) * 2 < (int64_t(1) << 31) && M * 4 <= (int64_t(1) << 31), "wide descriptor ranges", N, M);
+}
+long g_wide_launches = 0;
+hipError_t launch_ln_fwd_wide(int dtype, const RowPlan& p, const LnFwdArgs& a, hipStream_t) {
+  ++g_launches;
+  ++g_wide_launches;
+  check_wide_plan(p, false, dtype, a.M, a.stride, a.N, a.nvec, a.chunks, a.row_iters);
+  return hipSuccess;
+}
+hipError_t launch_ln_bwd_wide(int dtype, const RowPlan& p, const LnBwdArgs& a, hipStream_t) {
+  ++g_launches;
+  ++g_wide_launches;
+  check_wide_plan(p, true, dtype, a.M, a.stride, a.N, a.nvec, a.chunks, a.row_iters);
+  expect(!a.pipeline, "wide backward not pipelined");
   return hipSuccess;
 }
 hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t) {
@@ -157,12 +188,13 @@ void expect_ok(int st, const char* what, int64_t M, int64_t N) {
   if (st != RMSNORM_OK && g_bad <= 20) std::printf("   status %d: %s\n", st, rmsnorm_status_string(st));
 }
 
+void layernorms(int64_t M, int64_t N, int64_t stride, int dtype, int64_t off);
+
 void norms(int64_t M, int64_t N, int64_t stride, int dtype, int64_t mis) {
   const int es = elsize_of(dtype);
   const int64_t off = mis * es;  // element-aligned, possibly not 16-byte aligned
-  size_t wbytes = 0, lwbytes = 0;
+  size_t wbytes = 0;
   expect_ok(rmsnorm_bwd_workspace_bytes(M, N, dtype, &wbytes), "rms workspace query", M, N);
-  expect_ok(layernorm_bwd_workspace_bytes(M, N, dtype, &lwbytes), "ln workspace query", M, N);
   const hipStream_t s = nullptr;
   for (int flags : {0, int(RMSNORM_GEMMA), int(RMSNORM_GEMMA | RMSNORM_ROUND_NORMED)}) {
     expect_ok(rmsnorm_fwd(slot(0, off), slot(1), slot(2, off), reinterpret_cast<float*>(slot(3)), M, N, stride, 1e-6f,
@@ -185,6 +217,13 @@ void norms(int64_t M, int64_t N, int64_t stride, int dtype, int64_t mis) {
                 "rmsnorm_bwd_noalloc", M, N);
     }
   }
+  layernorms(M, N, stride, dtype, off);
+}
+
+void layernorms(int64_t M, int64_t N, int64_t stride, int dtype, int64_t off) {
+  size_t lwbytes = 0;
+  expect_ok(layernorm_bwd_workspace_bytes(M, N, dtype, &lwbytes), "ln workspace query", M, N);
+  const hipStream_t s = nullptr;
   expect_ok(layernorm_fwd(slot(0, off), slot(1), slot(8), slot(2, off), reinterpret_cast<float*>(slot(3)),
                           reinterpret_cast<float*>(slot(9)), M, N, stride, 1e-5f, dtype, s),
             "layernorm_fwd", M, N);
@@ -213,6 +252,33 @@ int main() {
       for (int64_t N : Ns)
         for (int64_t pad : {0, 1, 8, 64})
           for (int64_t mis : {0, 1}) norms(M, N, N + pad, dtype, mis);
+
+  // 16-bit LayerNorm rows beyond RMSNORM_N_MAX run in the wide kernels; fp32
+  // rows that long, and any row beyond LAYERNORM_N_MAX_16BIT, are rejected
+  for (int dtype = 1; dtype < 3; ++dtype)
+    for (int64_t M : {int64_t(0), int64_t(1), int64_t(255), int64_t(300), int64_t(65537), int64_t(1) << 20})
+      for (int64_t N : {int64_t(16385), int64_t(16392), int64_t(20000), int64_t(24576), int64_t(32767),
+                        int64_t(32768)})
+        for (int64_t pad : {0, 1, 8})
+          for (int64_t mis : {0, 1}) layernorms(M, N, N + pad, dtype, mis * 2);
+  expect(rmsn::g_wide_launches > 0, "wide launches checked");
+  {
+    const long before = g_launches;
+    size_t lw = 0;
+    for (int64_t N : {int64_t(16385), int64_t(32768)})
+      expect(layernorm_fwd(slot(0), slot(1), slot(8), slot(2), reinterpret_cast<float*>(slot(3)),
+                           reinterpret_cast<float*>(slot(9)), 4, N, N, 1e-5f, 0, nullptr) == RMSNORM_E_SHAPE &&
+                 layernorm_bwd_workspace_bytes(4, N, 0, &lw) == RMSNORM_E_SHAPE,
+             "fp32 LayerNorm rows beyond RMSNORM_N_MAX rejected", N);
+    for (int dtype = 1; dtype < 3; ++dtype)
+      expect(layernorm_fwd(slot(0), slot(1), slot(8), slot(2), reinterpret_cast<float*>(slot(3)),
+                           reinterpret_cast<float*>(slot(9)), 4, 32769, 32769, 1e-5f, dtype,
+                           nullptr) == RMSNORM_E_SHAPE &&
+                 rmsnorm_fwd(slot(0), slot(1), slot(2), reinterpret_cast<float*>(slot(3)), 4, 16385, 16385, 1e-6f,
+                             dtype, 0, nullptr) == RMSNORM_E_SHAPE,
+             "rows beyond each norm's limit rejected", dtype);
+    expect(g_launches == before, "no launch for a rejected row length");
+  }
 
   // RoPE: heads x head_dim per token, dense or a view of a wider (fused) row
   for (int dtype = 0; dtype < 3; ++dtype)

@@ -5,11 +5,16 @@
 // keeps the LDS combine buffer within 64 KB, and gives no row a wave that
 // lies wholly past N.  It also pins the row shapes
 // the planner picks for a few widths where the ordering of its rules
-// matters.  Built and run by tests/test_plan.py; prints one summary line and
-// exits non-zero on failure.
+// matters.  For 16-bit LayerNorm rows beyond RMSNORM_N_MAX (up to
+// LAYERNORM_N_MAX_16BIT) it checks that the wide plan covers the row within
+// the wide kernels' registers.  Built and
+// run by tests/test_plan.py; prints one summary line and exits non-zero on
+// failure.
 #include <cstdio>
 
 #include "host_plan.h"
+#include "launch.h"
+#include "layernorm.h"
 
 #include <cstring>
 #include <map>
@@ -73,6 +78,24 @@ int main(int argc, char** argv) {
               std::printf("bad plan: dtype=%d op=%d N=%ld vec=%d M=%ld iters=%d wpr=%d rpb=%d grid=%ld\n", dt,
                           static_cast<int>(op), static_cast<long>(N), vec, static_cast<long>(M), p.iters, p.wpr, p.rpb,
                           static_cast<long>(p.grid));
+          }
+        }
+  // 16-bit LayerNorm rows beyond the register plans: the wide kernels
+  static_assert(kLnWideMaxN == LAYERNORM_N_MAX_16BIT, "wide kernels cover every LayerNorm row");
+  for (int dt = 1; dt < 3; ++dt)
+    for (bool bwd : {false, true})
+      for (int64_t N = RMSNORM_N_MAX + 1; N <= LAYERNORM_N_MAX_16BIT; ++N)
+        for (int vec = 1; vec <= 8; vec *= 2) {
+          if (N % vec) continue;
+          for (int64_t M : {int64_t(1), int64_t(300), int64_t(1) << 20}) {
+            ++n;
+            const RowPlan p = plan_ln_wide(bwd, M, N, vec);
+            const bool ok = p.vec == vec && p.wpr * kWave == 1024 && p.rpb == 1 && p.iters >= 1 &&
+                            int64_t(p.iters) * 1024 * vec >= N && p.iters * vec <= kLnWideColsPerLane &&
+                            p.grid >= 1 && p.grid * p.row_iters >= M && (!bwd || p.grid <= partial_rows_bound(M));
+            if (!ok && bad++ < 10)
+              std::printf("bad wide plan: dtype=%d bwd=%d N=%ld vec=%d M=%ld chunks=%d grid=%ld\n", dt, int(bwd),
+                          static_cast<long>(N), vec, static_cast<long>(M), p.iters, static_cast<long>(p.grid));
           }
         }
   // (element size, N, op, waves per row, vectors per lane), 16-byte vectors

@@ -36,7 +36,10 @@ def test_fwd_rejections(L):
     assert fwd(L, dtype=3) == E_DTYPE
     assert fwd(L, M=-1) == E_SHAPE
     assert fwd(L, N=0) == E_SHAPE
-    assert fwd(L, N=16385) == E_SHAPE
+    # 16-bit rows up to 32768 elements (the wide kernels), fp32 rows up to 16384
+    assert fwd(L, N=32769) == E_SHAPE
+    assert fwd(L, N=32769, dtype=BF16) == E_SHAPE
+    assert fwd(L, N=16385, dtype=F32) == E_SHAPE
     assert fwd(L, stride=7) == E_STRIDE
     for eps in (0.0, -1e-5, float("inf"), float("nan")):
         assert fwd(L, eps=eps) == E_EPS
@@ -67,6 +70,10 @@ def test_workspace_query(L):
     assert out.value == 2 * 1024 * 8192 * 4  # two tables of at most 1024 fp32 partial rows
     assert L.layernorm_bwd_workspace_bytes(17, 257, F32, ctypes.byref(out)) == OK and out.value == 2 * 17 * 257 * 4
     assert L.layernorm_bwd_workspace_bytes(17, 0, F32, ctypes.byref(out)) == E_SHAPE
+    assert L.layernorm_bwd_workspace_bytes(17, 16385, F32, ctypes.byref(out)) == E_SHAPE
+    assert L.layernorm_bwd_workspace_bytes(17, 32769, F16, ctypes.byref(out)) == E_SHAPE
+    assert L.layernorm_bwd_workspace_bytes(300, 32768, BF16, ctypes.byref(out)) == OK
+    assert out.value == 2 * 300 * 32768 * 4
     assert L.layernorm_bwd_workspace_bytes(17, 8, 9, ctypes.byref(out)) == E_DTYPE
     assert L.layernorm_bwd_workspace_bytes(17, 8, F32, None) == E_NULL
     assert rn.layernorm_bwd_workspace_bytes(64, 128, 2) == 2 * 64 * 128 * 4
@@ -90,7 +97,8 @@ def bwd_rows(L, x=X, w=W, dy=DY, mu=MU, r=R, dx=DX, ws=WS, wsb=None, M=4, N=8, s
 def test_bwd_rejections(L, call):
     assert call(L, dtype=-1) == E_DTYPE
     assert call(L, N=0) == E_SHAPE
-    assert call(L, N=20000) == E_SHAPE
+    assert call(L, N=32769) == E_SHAPE
+    assert call(L, N=16385, dtype=F32) == E_SHAPE
     assert call(L, M=-2) == E_SHAPE
     assert call(L, stride=4) == E_STRIDE
     for kw in ("x", "w", "dy", "mu", "r", "dx", "ws"):
@@ -127,6 +135,7 @@ def test_bwd_specific_rejections(L):
 def test_dwdb_reduce_rejections(L):
     assert L.layernorm_dwdb_reduce(WS, -1, 8, DW, DB, None) == E_SHAPE
     assert L.layernorm_dwdb_reduce(WS, 4, 0, DW, DB, None) == E_SHAPE
+    assert L.layernorm_dwdb_reduce(WS, 4, 32769, DW, DB, None) == E_SHAPE
     assert L.layernorm_dwdb_reduce(WS, 1 << 15, 1 << 14, DW, DB, None) == E_SHAPE  # 2 * rows * N > 2^29
     # row counts whose 2 * rows * N wraps around int64 (to 0 for 1 << 61 rows x 4)
     assert L.layernorm_dwdb_reduce(WS, 1 << 61, 4, DW, DB, None) == E_SHAPE

@@ -65,10 +65,14 @@ def test_small_shapes(dtype, M, N):
 # counts where the forward grid is persistent with two multi-wave row groups
 # per workgroup (the last row step ragged for 8195 and 8200 rows); and
 # backward rows of 5-8 waves run as one workgroup of two or three row groups
-# per CU with the next row's loads in flight.  Each in place and not, with the
-# split and the fused backward.
+# per CU with the next row's loads in flight; rows of 1-4 waves where the
+# partial rows are a large share run one workgroup of their own shape per CU,
+# pipelined, as well.  Each in place and not, with the split and the fused
+# backward.
 LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16", 4100, 6144), ("f32", 3000, 4096),
-         ("f16", 4097, 8192), ("bf16", 4100, 8192), ("f16", 2049, 5120)]
+         ("f16", 4097, 8192), ("bf16", 4100, 8192), ("f16", 2049, 5120),
+         # rows of 1-4 waves, one workgroup per CU, next row's loads in flight
+         ("f16", 4100, 1024), ("f16", 4096, 2048), ("f16", 4096, 3072), ("f32", 4096, 2048), ("f16", 1000, 8192)]
 
 
 @pytest.mark.parametrize("dtype,M,N", LARGE, ids=[f"{d}-{m}x{n}" for d, m, n in LARGE])
@@ -78,6 +82,35 @@ def test_persistent_and_wide_workgroup_shapes(dtype, M, N):
     for split, in_place in ((True, False), (False, True)):
         _print_case(w.name, "split" if split else "fused", "in place" if in_place else "")
         compare_ln_with_oracle(LnRun(w, split_bwd=split, in_place=in_place))
+
+
+# 16-bit rows beyond 16384 elements, up to the chapter's 64 KB per row: the
+# wide kernels (one 1024-thread workgroup per row; 16-byte vectors held in
+# registers between the backward's passes, narrower ones read again; 32767
+# takes the most chunks, 32 one-element vectors per lane).  More rows than
+# the backward's 256 workgroups, so they loop; in place and not, split and
+# fused.
+WIDE = [("f16", 300, 16392), ("bf16", 257, 24576), ("f16", 33, 32768), ("bf16", 20, 32767), ("f16", 600, 20002),
+        ("bf16", 5, 16385), ("bf16", 513, 32768)]
+
+
+@pytest.mark.parametrize("dtype,M,N", WIDE, ids=[f"{d}-{m}x{n}" for d, m, n in WIDE])
+def test_wide_rows(dtype, M, N):
+    w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
+                    dy=wl.LN1.dy, eps=1e-5, seed=M * 13 + N)
+    for split, in_place in ((True, False), (False, True)):
+        _print_case(w.name, "split" if split else "fused", "in place" if in_place else "")
+        compare_ln_with_oracle(LnRun(w, split_bwd=split, in_place=in_place))
+
+
+def test_wide_rows_strided_and_misaligned():
+    for N, stride, offset in ((32768, 32800, 0), (20000, 20003, 1), (16400, 16408, 4)):
+        w = wl.LN1.scaled(M=40, N=N, dtype="bf16", seed=stride)
+        _print_case(w.name, "stride", stride, "offset", offset)
+        run = LnRun(w, row_stride=stride, offset=offset)
+        compare_ln_with_oracle(run)
+        pad = run.y.as_strided((w.M, stride - w.N), (stride, 1), run.y.storage_offset() + w.N)
+        assert torch.all(pad == -7.0)
 
 
 @pytest.mark.parametrize("N", [1024, 8192, 13312, 15872])

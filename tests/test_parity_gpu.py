@@ -125,6 +125,15 @@ SMALL = [
     ("bf16", 1500, 5120, True, False),  # 5 x 2, three row groups (15 waves)
     # persistent forward of 4-wave rows, two row groups per workgroup
     ("bf16", 8200, 4096, False, True),
+    # rows of 1-4 waves where the partial rows would be a large share: one
+    # workgroup of the row shape per CU, at least four row steps each where
+    # the grid keeps 8 waves per CU, the next row's loads in flight (2, 4, 5
+    # and 6 row steps, the odd counts with a ragged last step)
+    ("bf16", 4100, 2048, False, True),  # 2 x 2, four row groups per workgroup
+    ("f16", 4096, 1024, True, False),   # 1 x 2, eight row groups
+    ("bf16", 3000, 3072, False, False), # 3 x 2, two row groups (6 waves)
+    ("f32", 4097, 1024, False, True),   # fp32 4 x 1 x 2
+    ("bf16", 1151, 8192, True, True),   # 8 x 2 rows, 16-wave workgroups, 144 of them, 4 steps
 ]
 
 
