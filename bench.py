@@ -47,12 +47,13 @@ import workloads as wl  # noqa: E402
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
 METRIC = "RMSNorm fwd+bwd achieved HBM GB/s and % of peak, bf16 M=16384 N=8192"
-# the sources the RMSNorm kernels and their launch plans are built from (their
+# the sources every kernel and its launch plan are built from (their
 # fingerprint ties the committed counter summary to the code it was taken on;
 # comments excluded)
 KERNEL_SRCS = tuple(os.path.join(ROOT, "row_normalization_amd", "csrc", f)
-                    for f in ("rmsnorm_kernels.hip", "device_common.h", "launch.h", "host_plan.h"))
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_bwd_rows_c3_hbm_traffic.md")
+                    for f in ("rmsnorm_kernels.hip", "layernorm_kernels.hip", "elementwise_kernels.hip",
+                              "device_common.h", "launch.h", "host_plan.h"))
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_and_lds_all_kernels.md")
 
 
 def parse():
@@ -73,12 +74,18 @@ def parse():
                          "more than the 3.6 us reduction)")
     ap.add_argument("--samples", type=int, default=SAMPLES,
                     help=f"samples of {CALLS} back-to-back calls per per-launch or per-config figure (median)")
-    ap.add_argument("--no-configs", action="store_true", help="skip the five-workload protocol block")
+    ap.add_argument("--configs", nargs="*", default=sorted(wl.RMS_WORKLOADS), choices=sorted(wl.RMS_WORKLOADS),
+                    help="RMSNorm workloads of the per-workload protocol block (default: all five)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload protocol block")
     ap.add_argument("--no-layernorm", action="store_true", help="skip the LayerNorm sweep")
     ap.add_argument("--ln-samples", type=int, default=20, help="samples per LayerNorm sweep point and kernel")
     ap.add_argument("--ln-ns", type=int, nargs="*", default=None,
                     help="LayerNorm sweep points (N) to run; default: the chapter's 30 points")
     ap.add_argument("--no-elementwise", action="store_true", help="skip the RoPE and SwiGLU legs")
+    ap.add_argument("--counter-pass", metavar="MANIFEST",
+                    help="launch the fixed counter sequence (run under rocprofv3 --pmc) and write its manifest")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the counter summary of DIR/manifest.json and DIR/{fetch,write,lds} (no GPU)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the plain streaming kernels timed as the reference for the row kernels")
     return ap.parse_args()
@@ -98,17 +105,19 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(h: str):
-    """HBM bytes per backward-row-pass launch from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
+def traffic_table(h: str) -> dict:
+    """Calibrated HBM bytes per launch, by counter-pass label ("rms c3
+    bwd_rows", ...), from the committed counter summary, if it was taken on
+    the current kernel sources; else {}."""
     if not os.path.exists(PMC_SUMMARY):
-        return None
-    text = open(PMC_SUMMARY).read()
-    m_hash = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
-    m_bytes = re.search(r"scaled HBM bytes per launch:\s*`?([0-9]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != h:
-        return None
-    return int(m_bytes.group(1))
+        return {}
+    m = re.search(r"```json\n(.*?)\n```", open(PMC_SUMMARY).read(), flags=re.S)
+    if not m:
+        return {}
+    data = json.loads(m.group(1))
+    if data.get("kernel_sha") != h:
+        return {}
+    return {label: e["scaled_bytes"] for label, e in data["entries"].items()}
 
 
 class Path:
@@ -116,9 +125,11 @@ class Path:
 
     ``sets`` operand sets (x, dy, y, rstd, dx, workspace) share one gamma;
     call ``k`` uses set ``k % sets``, so rotating through enough sets keeps
-    every call's operands out of the caches.  Set 0 holds the generated
-    inputs, the others device copies of them.  Every call's arguments are
-    built once (a launch then costs one ctypes call on the host)."""
+    every call's operands out of the caches.  Every set is uploaded from the
+    generated host tensors (no device-to-device copy: under rocprofv3's
+    counter collection those crashed inside the runtime).  Every call's
+    arguments are built once (a launch then costs one ctypes call on the
+    host)."""
 
     def __init__(self, w: wl.Workload, sets: int = 1):
         import row_normalization_amd as rn
@@ -128,12 +139,12 @@ class Path:
         t = wl.make_inputs(w)
         dev = "cuda"
         self.gamma = t["gamma"].to(dev)
-        x0, dy0 = t["x"].to(dev), t["dy"].to(dev)
-        del t
         self.sets = sets
-        self.x = [x0] + [x0.clone() for _ in range(sets - 1)]
-        self.dy = [dy0] + [dy0.clone() for _ in range(sets - 1)]
-        self.dy_pristine = dy0.clone() if w.dx_in_place else None
+        self.x = [t["x"].to(dev) for _ in range(sets)]
+        self.dy = [t["dy"].to(dev) for _ in range(sets)]
+        self.dy_host = t["dy"] if w.dx_in_place else None
+        del t
+        x0, dy0 = self.x[0], self.dy[0]
         self.y = [torch.empty_like(x0) for _ in range(sets)]
         self.rstd = [torch.empty(w.M, dtype=torch.float32, device=dev) for _ in range(sets)]
         self.dx = self.dy if w.dx_in_place else [torch.empty_like(dy0) for _ in range(sets)]
@@ -182,9 +193,9 @@ class Path:
         """dy back to its generated values in every set (in place, dx overwrote
         it), then a read sweep so that the copies' dirty cache lines are
         written back before the timed calls."""
-        if self.dy_pristine is not None:
+        if self.dy_host is not None:
             for d in self.dy:
-                d.copy_(self.dy_pristine)
+                d.copy_(self.dy_host)
             flush_by_reading()
 
 
@@ -641,14 +652,194 @@ def stream_ceiling():
     return res
 
 
+# ---------------------------------------------------------------------------
+# Counter collection.  `--counter-pass MANIFEST` launches a fixed sequence
+# (COUNTER_CALLS launches of each kernel of each workload, then a plain copy
+# of COPY_BYTES for calibration) under rocprofv3 --pmc, one counter set per
+# run, and writes the sequence to MANIFEST; `--summarize-counters DIR` then
+# attributes the dispatches of DIR/{fetch,write,lds}/*counter_collection.csv
+# to it in launch order and prints the summary committed under profiles/.
+# ---------------------------------------------------------------------------
+COUNTER_CALLS = 3
+COPY_BYTES = 256 << 20
+COPY_KERNEL = "elementwise_kernel"  # torch.neg(a, out=b): reads a, writes b
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD",
+                "SQ_INSTS_VMEM_WR", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def counter_workloads() -> list:
+    """(label prefix, kind, workload) of the counter pass, in launch order."""
+    out = [(f"rms {k}", "rms", wl.RMS_WORKLOADS[k]) for k in ("c2", "c3", "c4", "c5")]
+    out += [(f"ln {n}", "ln", wl.ln_sweep(n)) for n in (1024, 4096, 8192)]
+    out.append(("ln unit-test", "ln", wl.LN1))
+    out.append(("ln wide", "ln", wl.ln_sweep(8192).scaled(N=32768, name="ln_f16_4096x32768",
+                                                             note="16-bit rows beyond 16384 (wide kernels)")))
+    return out
+
+
+def counter_pass(manifest: str) -> None:
+    import row_normalization_amd as rn
+
+    entries = []
+
+    def launch(label, kernel, fn, nbytes, scratch=0, workload=""):
+        for _ in range(COUNTER_CALLS):
+            fn()
+        torch.cuda.synchronize()
+        entries.append({"label": label, "kernel": kernel, "calls": COUNTER_CALLS, "algorithmic_bytes": int(nbytes),
+                        "scratch_bytes": int(scratch), "workload": workload})
+        print(f"[counters] {label}", file=sys.stderr, flush=True)
+
+    for prefix, kind, w in counter_workloads():
+        if kind == "rms":
+            path = Path(w)  # its set-up runs one backward row pass
+            b = wl.algorithmic_bytes(w.M, w.N, w.elsize)
+            part = path.partial_rows * w.N * 4
+            launch(f"{prefix} fwd", "rmsnorm_fwd_kernel", path.fwd, b["fwd"], 0, w.name)
+            launch(f"{prefix} bwd_rows", "rmsnorm_bwd_rows_kernel", path.bwd_rows, b["bwd_rows"], part, w.name)
+            launch(f"{prefix} reduce", "rmsnorm_dgamma_reduce_kernel", path.reduce, 4 * w.N, part, w.name)
+        else:
+            path = LnPath(w)
+            b = wl.ln_algorithmic_bytes(w.M, w.N, w.elsize)
+            wide = w.N > 16384  # 16-bit rows beyond the register plans
+            launch(f"{prefix} fwd", "layernorm_fwd_wide_kernel" if wide else "layernorm_fwd_kernel", path.fwd,
+                   b["fwd"], 0, w.name)
+            path.bwd_rows()  # the partial-row count, before the counted launches
+            torch.cuda.synchronize()
+            part = 2 * path.partial_rows * w.N * 4
+            launch(f"{prefix} bwd_rows", "layernorm_bwd_wide_kernel" if wide else "layernorm_bwd_rows_kernel",
+                   path.bwd_rows, b["bwd_rows"], part, w.name)
+            launch(f"{prefix} reduce", "rmsnorm_dgamma_reduce_kernel", path.reduce, 8 * w.N, part, w.name)
+        del path
+        torch.cuda.empty_cache()
+
+    r = wl.ROPE1
+    t = wl.make_rope_inputs(r)
+    q, cos, sin, pos = t["q"].cuda(), t["cos"].cuda(), t["sin"].cuda(), t["positions"].cuda()
+    L, stream = rn.lib(), torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), r.tokens, r.heads, r.head_dim, r.heads * r.head_dim, cos.data_ptr(), sin.data_ptr(),
+            r.seq_len, pos.data_ptr(), r.seq_len, DTYPE_CODE[r.dtype], stream)
+    nb = wl.rope_algorithmic_bytes(r.tokens, r.heads, r.head_dim, r.elsize, r.seq_len)
+    launch("rope fwd", "rope_kernel", lambda: L.rope_fwd(*args), nb, 0, r.name)
+    launch("rope bwd", "rope_kernel", lambda: L.rope_bwd(*args), nb, 0, r.name)
+    del q, cos, sin, pos, t
+
+    g = wl.SWIGLU1
+    t = wl.make_swiglu_inputs(g)
+    e, gg, dh = (t[k].cuda() for k in ("e", "g", "dh"))
+    h, df, de = (torch.empty_like(e) for _ in range(3))
+    code = DTYPE_CODE[g.dtype]
+    b = wl.swiglu_algorithmic_bytes(g.M, g.N, g.elsize)
+    launch("swiglu fwd", "swiglu_fwd_kernel",
+           lambda: L.swiglu_fwd(e.data_ptr(), gg.data_ptr(), h.data_ptr(), g.M, g.N, g.N, code, stream), b["fwd"], 0,
+           g.name)
+    launch("swiglu bwd", "swiglu_bwd_kernel",
+           lambda: L.swiglu_bwd(dh.data_ptr(), e.data_ptr(), gg.data_ptr(), h.data_ptr(), df.data_ptr(),
+                                de.data_ptr(), g.M, g.N, g.N, code, stream), b["bwd"], 0, g.name)
+    del e, gg, dh, h, df, de, t
+    torch.cuda.empty_cache()
+
+    a = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty_like(a)
+    launch("copy", COPY_KERNEL, lambda: torch.neg(a, out=c), 2 * COPY_BYTES, 0, f"{COPY_BYTES >> 20} MiB bf16 negation")
+    with open(manifest, "w") as f:
+        json.dump({"kernel_sha": kernel_hash(), "entries": entries}, f, indent=1)
+
+
+def _dispatches(csv_dir: str) -> list:
+    """[(dispatch id, kernel name, grid, workgroup, {counter: value})] of the
+    counter_collection.csv under csv_dir, in dispatch order."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {csv_dir}, found {files}")
+    rows = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            d = rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]),
+                                                        int(r["Workgroup_Size"]), {}])
+            d[3][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [(k, *rows[k]) for k in sorted(rows)]
+
+
+def _attribute(entries: list, dispatches: list) -> list:
+    """For each manifest entry, its `calls` dispatches: the next ones in
+    dispatch order whose kernel name matches (other launches are skipped)."""
+    out, i = [], 0
+    for e in entries:
+        got = []
+        while len(got) < e["calls"]:
+            if i >= len(dispatches):
+                raise SystemExit(f"ran out of dispatches looking for {e['label']} ({e['kernel']})")
+            if e["kernel"] in dispatches[i][1]:
+                got.append(dispatches[i])
+            i += 1
+        out.append(got)
+    return out
+
+
+def summarize_counters(d: str) -> None:
+    """Print the markdown counter summary of the runs under d (see above)."""
+    man = json.load(open(os.path.join(d, "manifest.json")))
+    entries = man["entries"]
+    per = {}
+    for run in ("fetch", "write", "lds"):
+        if os.path.isdir(os.path.join(d, run)):
+            per[run] = _attribute(entries, _dispatches(os.path.join(d, run)))
+    med = lambda run, k, c: float(np.median([x[4][c] for x in per[run][k]]))
+    copy = next(k for k, e in enumerate(entries) if e["label"] == "copy")
+    half = COPY_BYTES
+    f_scale = half / (med("fetch", copy, "FETCH_SIZE") * 1024)
+    w_scale = half / (med("write", copy, "WRITE_SIZE") * 1024)
+    table = {}
+    lines = []
+    for k, e in enumerate(entries):
+        fetch_kib, write_kib = med("fetch", k, "FETCH_SIZE"), med("write", k, "WRITE_SIZE")
+        rd, wr = fetch_kib * 1024 * f_scale, write_kib * 1024 * w_scale
+        need = e["algorithmic_bytes"] + e["scratch_bytes"]
+        grid, wg = per["fetch"][k][0][2], per["fetch"][k][0][3]
+        row = {"kernel": e["kernel"], "workload": e["workload"], "grid": grid, "workgroup": wg,
+               "fetch_kib": round(fetch_kib, 1), "write_kib": round(write_kib, 1), "scaled_bytes": int(rd + wr),
+               "algorithmic_bytes": e["algorithmic_bytes"], "scratch_bytes": e["scratch_bytes"],
+               "ratio": round((rd + wr) / need, 4)}
+        if "lds" in per:
+            for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAVES"):
+                row[c] = med("lds", k, c)
+        table[e["label"]] = row
+        lines.append(f"| {e['label']} | {e['kernel']} | {grid} / {wg} | {fetch_kib:.1f} | {write_kib:.1f} | "
+                     f"{rd / 1e6:.2f} | {wr / 1e6:.2f} | {e['algorithmic_bytes'] / 1e6:.2f} | "
+                     f"{e['scratch_bytes'] / 1e6:.2f} | {(rd + wr) / need:.3f} | "
+                     + (" | ".join(f"{row[c]:.0f}" for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                                                               "SQ_INSTS_LDS")) if "lds" in per else "- | - | -")
+                     + " |")
+    print("| Launch | Kernel | Grid / workgroup (threads) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | Read (MB) | "
+          "Written (MB) | Algorithmic (MB) | Scratch (MB) | Moved / (algorithmic + scratch) | "
+          "SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE | SQ_INSTS_LDS |")
+    print("|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    print("\n".join(lines))
+    print()
+    print(f"Calibration: the copy reads and writes {COPY_BYTES} bytes; read bytes = FETCH_SIZE x 1024 x "
+          f"{f_scale:.4f}, written bytes = WRITE_SIZE x 1024 x {w_scale:.4f}.")
+    print()
+    print("```json")
+    print(json.dumps({"kernel_sha": man["kernel_sha"], "fetch_scale": round(f_scale, 5),
+                      "write_scale": round(w_scale, 5), "entries": table}))
+    print("```")
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this path is measured on a single MI355X; "
               "multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
     # before torch initialises the GPU in this process
-    ceiling = None if args.no_ceiling else stream_ceiling()
+    ceiling = None if args.no_ceiling or args.counter_pass else stream_ceiling()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -659,6 +850,9 @@ def main():
 
         __graft_entry__.build()
     torch.cuda.set_device(0)
+    if args.counter_pass:
+        counter_pass(args.counter_pass)
+        return
     w = wl.RMS_WORKLOADS[args.workload]
     path = Path(w)
     overlapped = OverlappedSteps(path)
@@ -691,7 +885,8 @@ def main():
     t_rows = kern["bwd_rows"]["median_s"]
     achieved = b["bwd_rows"] / t_rows / 1e9
     h = kernel_hash()
-    traffic = traffic_from_profile(h)
+    traffic_tab = traffic_table(h)
+    traffic = traffic_tab.get(f"rms {args.workload} bwd_rows")
     copy_gbps = copy_reference(256 << 20, 50)
     out = {
         "metric": METRIC,
@@ -734,15 +929,23 @@ def main():
     del overlapped, path, schedules
     torch.cuda.empty_cache()
     out["configs"] = None if args.no_configs else {k: config_protocol(wl.RMS_WORKLOADS[k], args.samples)
-                                                  for k in sorted(wl.RMS_WORKLOADS)}
+                                                  for k in args.configs}
     out["layernorm"] = None if args.no_layernorm else layernorm_sweep(args.ln_samples, args.ln_ns)
+    # calibrated HBM bytes per launch from the committed counter summary (None
+    # where it holds no such launch or was taken on other kernel sources)
+    for k, c in (out["configs"] or {}).items():
+        c["traffic_bytes"] = {leg: traffic_tab.get(f"rms {k} {leg}") for leg in ("fwd", "bwd_rows", "reduce")}
+    for pt in (out["layernorm"] or {}).get("points", []):
+        pt["traffic_bytes"] = {leg: traffic_tab.get(f"ln {pt['N']} {leg}") for leg in ("fwd", "bwd_rows", "reduce")}
     if args.no_elementwise:
         out["rope"] = out["swiglu"] = None
     else:
         out["rope"] = rope_leg(args.samples)
+        out["rope"]["traffic_bytes"] = {leg: traffic_tab.get(f"rope {leg}") for leg in ("fwd", "bwd")}
         print(f"[rope] {out['rope']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         out["swiglu"] = swiglu_leg(args.samples)
+        out["swiglu"]["traffic_bytes"] = {leg: traffic_tab.get(f"swiglu {leg}") for leg in ("fwd", "bwd")}
         print(f"[swiglu] {out['swiglu']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
