@@ -27,19 +27,41 @@ constexpr int dtype_code() {
   return sizeof(S) == 4 ? 0 : std::is_same<S, _Float16>::value ? 2 : 1;
 }
 
-// Index of element e of vector v in an LDS table of nvec vectors of VEC
-// floats (the LayerNorm backward's row-group combine), laid out as VEC / 4
-// planes of nvec four-float cells (one plane of VEC-float cells for VEC < 4):
+// An LDS table of nvec vectors of VEC floats (the LayerNorm backward's
+// row-group combine), laid out as VEC / 4 planes of nvec four-float cells (one plane of VEC-float cells for VEC < 4):
 // a wave's 16-byte accesses then cover consecutive addresses, free of bank
 // conflicts, where VEC = 8 consecutive floats per lane (a 32-byte lane
 // stride) conflict.  Measured on MI355X: LayerNorm fp16 backward 1-5 %
 // faster (4096 x 1024-8192, 1151 x 8192); the RMSNorm combine, whose
 // conflicts were few, was 1-5 % slower with it at N = 1024 and keeps VEC
 // consecutive floats per vector.
+// Cells are moved as whole 16-byte (8-, 4-byte) LDS accesses: written
+// element by element, with the other table's stores in between, they would
+// become single-float accesses, as the compiler cannot tell that the two
+// tables do not overlap.
 template <int VEC>
-__device__ __forceinline__ int comb_index(int v, int e, int nvec) {
+__device__ __forceinline__ void comb_store(float* table, int v, int nvec, const float (&x)[VEC]) {
   constexpr int kCell = VEC < 4 ? VEC : 4;
-  return (e / kCell) * (nvec * kCell) + v * kCell + e % kCell;
+  typedef float cell_t __attribute__((ext_vector_type(kCell)));
+#pragma unroll
+  for (int h = 0; h < VEC / kCell; ++h) {
+    cell_t c;
+#pragma unroll
+    for (int e = 0; e < kCell; ++e) c[e] = x[h * kCell + e];
+    *reinterpret_cast<cell_t*>(table + (h * nvec + v) * kCell) = c;
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void comb_load(const float* table, int v, int nvec, float (&x)[VEC]) {
+  constexpr int kCell = VEC < 4 ? VEC : 4;
+  typedef float cell_t __attribute__((ext_vector_type(kCell)));
+#pragma unroll
+  for (int h = 0; h < VEC / kCell; ++h) {
+    const cell_t c = *reinterpret_cast<const cell_t*>(table + (h * nvec + v) * kCell);
+#pragma unroll
+    for (int e = 0; e < kCell; ++e) x[h * kCell + e] = c[e];
+  }
 }
 
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family:
