@@ -333,6 +333,22 @@ inline bool bwd_pipelined(RowOp op, const RowPlan& p, int dtype) {
   return alone_on_cu && bwd_pipeline_fits(op, dtype, p.vec, p.iters);
 }
 
+// Whether the backward writes its partial rows (tables x grid x N fp32)
+// with the nontemporal policy: where they are kPartialsNtBytes or more, so
+// they do not take the place of the rows' own data in the caches, above all
+// the 256 MB Infinity Cache, which at M = 4096 holds most of a LayerNorm
+// backward's x, dy and dx.  Measured on MI355X (interleaved comparison, full
+// backward): LayerNorm fp16 4096 x 4096 (8 MiB of partials) 6.3 %, 4096 x
+// 8192 5.3 %, 1151 x 8192 6.5 %, RMSNorm bf16 2048 x 8192 4.6 %, 4096 x 4096
+// (4 MiB) 1.6 % faster, 16384 x 8192 and 8192 x 16384 within 0.4 %; at
+// LayerNorm 4096 x 1024 (2 MiB), which the column sum reads back from the
+// caches, 4.2 % slower, and in the wide LayerNorm kernels (4096 x 24576 and
+// 4096 x 32768, 48-64 MiB) 3.5 % slower, so those keep the default policy.
+constexpr int64_t kPartialsNtBytes = int64_t(4) << 20;
+inline bool partials_nontemporal(int tables, int64_t grid, int64_t N) {
+  return static_cast<int64_t>(tables) * grid * N * 4 >= kPartialsNtBytes;
+}
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_E_HIP; }
 
 }  // namespace rmsn

@@ -63,7 +63,8 @@ struct BwdArgs {
   int32_t wpr;
   int32_t rpb;
   int64_t row_iters;
-  int32_t pipeline;  // 1: keep the next row's loads in flight during a row's work
+  int32_t pipeline;     // 1: keep the next row's loads in flight during a row's work
+  int32_t partials_nt;  // 1: write the partial rows with the nontemporal policy (partials_nontemporal)
 };
 
 // Column sums of one or two [rows, N] fp32 tables stored back to back
@@ -115,8 +116,9 @@ struct LnBwdArgs {
   int32_t wpr;
   int32_t rpb;
   int64_t row_iters;
-  int32_t pipeline;  // as in BwdArgs
-  int32_t chunks;    // wide rows only: 1024-vector chunks per row
+  int32_t pipeline;     // as in BwdArgs
+  int32_t partials_nt;  // as in BwdArgs
+  int32_t chunks;       // wide rows only: 1024-vector chunks per row
 };
 
 // LayerNorm rows of 16-bit elements beyond the register plans (up to

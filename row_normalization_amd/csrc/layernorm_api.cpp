@@ -77,6 +77,7 @@ int launch_ln_bwd_rows_checked(const void* x, const void* weight, const void* dy
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
   a.pipeline = wide ? 0 : bwd_pipelined(RowOp::kLnBwd, p, dtype);
+  a.partials_nt = !wide && partials_nontemporal(2, p.grid, N);
   a.chunks = wide ? p.iters : 0;
   const int st = hip_status(wide ? launch_ln_bwd_wide(dtype, p, a, stream) : launch_ln_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;

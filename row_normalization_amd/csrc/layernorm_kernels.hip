@@ -404,10 +404,18 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
   const Rsrc rdb = make_rsrc(pb, static_cast<uint32_t>(a.N) * 4u);
   const uint32_t voff32 = L.first_vec() * VEC * 4u;
   const uint32_t iter32 = static_cast<uint32_t>(a.wpr) * kWave * VEC * 4u;
+  if (a.partials_nt) {
 #pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
-    buf_store_f32<VEC, kDefault>(accw[i], rdw, voff32 + i * iter32);
-    buf_store_f32<VEC, kDefault>(accb[i], rdb, voff32 + i * iter32);
+    for (int i = 0; i < ITERS; ++i) {
+      buf_store_f32<VEC, kNontemporal>(accw[i], rdw, voff32 + i * iter32);
+      buf_store_f32<VEC, kNontemporal>(accb[i], rdb, voff32 + i * iter32);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      buf_store_f32<VEC, kDefault>(accw[i], rdw, voff32 + i * iter32);
+      buf_store_f32<VEC, kDefault>(accb[i], rdb, voff32 + i * iter32);
+    }
   }
 }
 
@@ -595,8 +603,13 @@ __global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_kernel(const 
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     const uint32_t o = k < chunks ? (k * kWideThreads + threadIdx.x) * VEC * 4u : kOutOfRange;
-    buf_store_f32<VEC, kDefault>(accw[k], rpw, o);
-    buf_store_f32<VEC, kDefault>(accb[k], rpb, o);
+    if (a.partials_nt) {
+      buf_store_f32<VEC, kNontemporal>(accw[k], rpw, o);
+      buf_store_f32<VEC, kNontemporal>(accb[k], rpb, o);
+    } else {
+      buf_store_f32<VEC, kDefault>(accw[k], rpw, o);
+      buf_store_f32<VEC, kDefault>(accb[k], rpb, o);
+    }
   }
 }
 

@@ -84,6 +84,7 @@ int launch_bwd_rows_checked(const void* x, const void* gamma, const void* dy, co
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
   a.pipeline = bwd_pipelined(RowOp::kRmsBwd, p, dtype);
+  a.partials_nt = partials_nontemporal(1, p.grid, N);
   const int st = hip_status(launch_bwd_rows(dtype, p, a, stream));
   if (st == RMSNORM_OK) *rows_written = p.grid;
   return st;

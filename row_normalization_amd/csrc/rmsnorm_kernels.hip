@@ -320,8 +320,13 @@ __global__ __launch_bounds__(1024) void rmsnorm_bwd_rows_kernel(const BwdArgs a)
       }
     }
   }
+  if (a.partials_nt) {
 #pragma unroll
-  for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kDefault>(acc[i], rp, voff32 + i * iter32);
+    for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kNontemporal>(acc[i], rp, voff32 + i * iter32);
+  } else {
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) buf_store_f32<VEC, kDefault>(acc[i], rp, voff32 + i * iter32);
+  }
 }
 
 // ---------------------------------------------------------------------------

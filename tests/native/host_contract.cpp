@@ -84,6 +84,7 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
                          (p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits)),
          "pipelined only where it fits and the workgroup is alone on its CU");
   expect(p.grid <= partial_rows_bound(a.M), "partial rows within the workspace", p.grid);
+  expect(a.partials_nt == int(partials_nontemporal(1, p.grid, a.N)), "partial-row store policy", p.grid, a.N);
   expect(reinterpret_cast<const char*>(a.partials) != kScratch ||
              p.grid * int64_t(a.N) * 4 <= RMSNORM_STATIC_SCRATCH_BYTES,
          "partial rows within the static scratch", p.grid, a.N);
@@ -107,6 +108,7 @@ hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, h
   ++g_launches;
   check_row_plan(p, RowOp::kLnBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 8 <= 65536, "LDS combine size", a.N);
+  expect(a.partials_nt == int(partials_nontemporal(2, p.grid, a.N)), "partial-row store policy", p.grid, a.N);
   expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kLnBwd, dtype, p.vec, p.iters) &&
                          (p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits)),
          "pipelined only where it fits and the workgroup is alone on its CU");
@@ -139,6 +141,7 @@ hipError_t launch_ln_bwd_wide(int dtype, const RowPlan& p, const LnBwdArgs& a, h
   ++g_wide_launches;
   check_wide_plan(p, true, dtype, a.M, a.stride, a.N, a.nvec, a.chunks, a.row_iters);
   expect(!a.pipeline, "wide backward not pipelined");
+  expect(!a.partials_nt, "wide partial rows with the default policy");
   return hipSuccess;
 }
 hipError_t launch_rope(int dtype, int vec, const RopeArgs& a, hipStream_t) {
