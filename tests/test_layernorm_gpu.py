@@ -242,6 +242,44 @@ def test_autograd_gradients(dtype):
         assert err.max() <= tol, (name, err.max())
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 20000), ("f16", 32768)])
+def test_autograd_wide_rows(dtype, N):
+    """The adapter on rows beyond 16384 elements (the wide kernels)."""
+    w = wl.LN1.scaled(M=6, N=N, dtype=dtype, seed=13)
+    _print_case("autograd wide", w.name)
+    t = wl.make_inputs(w)
+    x = t["x"].cuda().view(2, 3, N).requires_grad_(True)
+    wt = t["gamma"].cuda().requires_grad_(True)
+    b = t["beta"].cuda().requires_grad_(True)
+    y = rn.layernorm(x, (N,), wt, b, 1e-5)
+    y.backward(t["dy"].cuda().view(2, 3, N))
+    xo, wo, bo, dyo = (wl.to_f64(t[k]) for k in ("x", "gamma", "beta", "dy"))
+    y_o, _, r_o = lo.forward(xo, wo, bo, 1e-5)
+    dx_o, dw_o, db_o = lo.backward(xo, wo, dyo, 1e-5)
+    from tests.parity import check_close
+
+    check_close("y", wl.to_f64(y).reshape(6, N), y_o, dtype, "y")
+    check_close("dx", wl.to_f64(x.grad).reshape(6, N), dx_o, dtype, "dx", direct=wo * dyo * r_o[:, None])
+    tol = {"bf16": 8e-3, "f16": 1e-3}[dtype]
+    for name, g, o in (("dw", wt.grad, dw_o), ("db", b.grad, db_o)):
+        err = np.abs(wl.to_f64(g) - o) / (np.abs(o) + np.sqrt(np.mean(o ** 2)))
+        assert err.max() <= tol, (name, err.max())
+
+
+def test_zero_rows_wide():
+    """M = 0 with a wide row: a no-op forward, zero weight gradients."""
+    N = 20000
+    dw = torch.full((N,), float("nan"), device="cuda")
+    db = torch.full((N,), float("nan"), device="cuda")
+    x, y = (torch.empty(0, N, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    wt, bias = (torch.ones(N, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    mean, rstd = (torch.empty(0, device="cuda") for _ in range(2))
+    rn.layernorm_fwd(x, wt, bias, y, mean, rstd, eps=1e-5)
+    rn.layernorm_bwd(x, wt, x, mean, rstd, x, dw, db, torch.empty(1, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0) and torch.all(db == 0)
+
+
 def test_module_training_matches_fp64_reference():
     """A few SGD steps through the LayerNorm module on fp32 data track the same
     steps through torch's LayerNorm in CPU float64."""

@@ -8,6 +8,10 @@ N + pad with pad in {0, 1, 8, 64, 333}; a base offset of 0, 1 or 3 elements
 dx written over dy, and the split (row pass + reduction) or fused backward.  The tolerances are
 those of ``tests.parity`` and ``tests.parity_ln``.
 
+16-bit LayerNorm rows beyond 16384 elements (the wide kernels) get their own
+seeded cases: N uniform in [16385, 32768], M log-uniform in [1, 600], the
+same strides, offsets, in-place and split choices.
+
 Wider random runs of the same kind (several thousand cases) met the fp32
 rounding limits of two-column LayerNorm rows whose spread is near sqrt(eps)
 and of one-column RMSNorm rows; those cases are kept here with their seeds.
@@ -124,3 +128,29 @@ def test_large_random_case(case):
         w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
                         dy=wl.LN1.dy, eps=1e-5, seed=M + N)
         compare_ln_with_oracle(LnRun(w, split_bwd=split, in_place=in_place))
+
+
+def _wide_cases(seed: int, n: int):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < n:
+        N = int(rng.integers(16385, 32769))
+        M = max(1, int(np.exp(rng.uniform(0.0, np.log(600.0)))))
+        dtype = str(rng.choice(["bf16", "f16"]))
+        pad = int(rng.choice([0, 0, 1, 8, 64, 333]))
+        offset = int(rng.choice([0, 0, 1, 3]))
+        in_place, split = (bool(v) for v in rng.integers(0, 2, size=2))
+        out.append((dtype, M, N, pad, offset, False, in_place, split))
+    return out
+
+
+WIDE_CASES = _wide_cases(32768, 16)
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[_id(c) for c in WIDE_CASES])
+def test_layernorm_wide_random_case(case):
+    dtype, M, N, pad, offset, _, in_place, split = case
+    print("case:", _id(case), flush=True)
+    w = wl.Workload(f"ln_{dtype}_{M}x{N}", dtype, M, N, x=wl.LN1.x, gamma=wl.LN1.gamma, beta=wl.LN1.beta,
+                    dy=wl.LN1.dy, eps=1e-5, seed=M * 7 + N)
+    compare_ln_with_oracle(LnRun(w, row_stride=N + pad, offset=offset, split_bwd=split, in_place=in_place))
