@@ -169,13 +169,21 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
 // kBwdMinGridWaves / 256 waves was slower (4096 x 1024 with 128 workgroups
 // of 8 waves: 13 %).
 constexpr double kBwdWideShare = 0.03;
+// Where the pipelined loop is not compiled for the plan (bf16 LayerNorm, whose
+// unpacking needs more registers; narrower vectors), only rows of 4-8 waves
+// run one 16-wave workgroup per CU (two to four row groups keep each other's
+// loads in flight), and only above kBwdWideShareUnpipelined.  Measured on
+// MI355X, LayerNorm bf16 full backward: 4096 x 4096 (share 0.33) 9 %, 4096 x
+// 8192 (0.17) 3 %, 4096 x 6144 (0.17) 1.8 %, 1151 x 8192 (0.59) 21 % faster;
+// 16384 x 6432 (0.042) 5 % slower; rows of 1-3 waves (4096 x 1024-3072, 16
+// row groups to combine) 0.5-22 % slower, as was fp32 RMSNorm 4096 x 1001.
+constexpr double kBwdWideShareUnpipelined = 0.1;
 constexpr int64_t kBwdMinSteps = 4;
 constexpr int64_t kBwdMinGridWaves = 2048;
 
-inline bool bwd_partials_heavy(RowOp op, int64_t M, int es, int64_t grid) {
+inline bool bwd_partials_heavy(RowOp op, int64_t M, int es, int64_t grid, double share = kBwdWideShare) {
   const int tables = op == RowOp::kLnBwd ? 2 : 1;
-  return static_cast<double>(tables) * static_cast<double>(grid) * 4.0 >
-         kBwdWideShare * 3.0 * static_cast<double>(M) * es;
+  return static_cast<double>(tables) * static_cast<double>(grid) * 4.0 > share * 3.0 * static_cast<double>(M) * es;
 }
 
 // Row shapes the rule above does not pick, where an interleaved comparison on
@@ -265,6 +273,12 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
       p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
       groups = ceil_div(M, p.rpb);
     }
+    per_cu = 1;
+  } else if (backward && p.wpr * 2 >= kBlockWaves && p.wpr <= kBlockWaves &&
+             bwd_partials_heavy(op, M, es, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)),
+                                kBwdWideShareUnpipelined)) {
+    p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
+    groups = ceil_div(M, p.rpb);
     per_cu = 1;
   }
   // The forward is persistent where that grid fills every CU with

@@ -72,7 +72,9 @@ def test_small_shapes(dtype, M, N):
 LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16", 4100, 6144), ("f32", 3000, 4096),
          ("f16", 4097, 8192), ("bf16", 4100, 8192), ("f16", 2049, 5120),
          # rows of 1-4 waves, one workgroup per CU, next row's loads in flight
-         ("f16", 4100, 1024), ("f16", 4096, 2048), ("f16", 4096, 3072), ("f32", 4096, 2048), ("f16", 1000, 8192)]
+         ("f16", 4100, 1024), ("f16", 4096, 2048), ("f16", 4096, 3072), ("f32", 4096, 2048), ("f16", 1000, 8192),
+         # bf16 rows of 4-8 waves, not pipelined: one 16-wave workgroup per CU
+         ("bf16", 4096, 4096), ("bf16", 1151, 8192), ("bf16", 4097, 6144)]
 
 
 @pytest.mark.parametrize("dtype,M,N", LARGE, ids=[f"{d}-{m}x{n}" for d, m, n in LARGE])
