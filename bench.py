@@ -686,12 +686,12 @@ def counter_pass(manifest: str) -> None:
 
     entries = []
 
-    def launch(label, kernel, fn, nbytes, scratch=0, workload=""):
+    def launch(label, kernel, fn, nbytes, scratch=0, workload="", elements=0):
         for _ in range(COUNTER_CALLS):
             fn()
         torch.cuda.synchronize()
         entries.append({"label": label, "kernel": kernel, "calls": COUNTER_CALLS, "algorithmic_bytes": int(nbytes),
-                        "scratch_bytes": int(scratch), "workload": workload})
+                        "scratch_bytes": int(scratch), "workload": workload, "elements": int(elements)})
         print(f"[counters] {label}", file=sys.stderr, flush=True)
 
     for prefix, kind, w in counter_workloads():
@@ -699,20 +699,21 @@ def counter_pass(manifest: str) -> None:
             path = Path(w)  # its set-up runs one backward row pass
             b = wl.algorithmic_bytes(w.M, w.N, w.elsize)
             part = path.partial_rows * w.N * 4
-            launch(f"{prefix} fwd", "rmsnorm_fwd_kernel", path.fwd, b["fwd"], 0, w.name)
-            launch(f"{prefix} bwd_rows", "rmsnorm_bwd_rows_kernel", path.bwd_rows, b["bwd_rows"], part, w.name)
+            launch(f"{prefix} fwd", "rmsnorm_fwd_kernel", path.fwd, b["fwd"], 0, w.name, w.M * w.N)
+            launch(f"{prefix} bwd_rows", "rmsnorm_bwd_rows_kernel", path.bwd_rows, b["bwd_rows"], part, w.name,
+                   w.M * w.N)
             launch(f"{prefix} reduce", "rmsnorm_dgamma_reduce_kernel", path.reduce, 4 * w.N, part, w.name)
         else:
             path = LnPath(w)
             b = wl.ln_algorithmic_bytes(w.M, w.N, w.elsize)
             wide = w.N > 16384  # 16-bit rows beyond the register plans
             launch(f"{prefix} fwd", "layernorm_fwd_wide_kernel" if wide else "layernorm_fwd_kernel", path.fwd,
-                   b["fwd"], 0, w.name)
+                   b["fwd"], 0, w.name, w.M * w.N)
             path.bwd_rows()  # the partial-row count, before the counted launches
             torch.cuda.synchronize()
             part = 2 * path.partial_rows * w.N * 4
             launch(f"{prefix} bwd_rows", "layernorm_bwd_wide_kernel" if wide else "layernorm_bwd_rows_kernel",
-                   path.bwd_rows, b["bwd_rows"], part, w.name)
+                   path.bwd_rows, b["bwd_rows"], part, w.name, w.M * w.N)
             launch(f"{prefix} reduce", "rmsnorm_dgamma_reduce_kernel", path.reduce, 8 * w.N, part, w.name)
         del path
         torch.cuda.empty_cache()
@@ -765,6 +766,7 @@ def _dispatches(csv_dir: str) -> list:
             d = rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]),
                                                         int(r["Workgroup_Size"]), {}])
             d[3][r["Counter_Name"]] = float(r["Counter_Value"])
+            d[3]["VGPR_Count"] = float(r.get("VGPR_Count") or 0)
     return [(k, *rows[k]) for k in sorted(rows)]
 
 
@@ -804,24 +806,31 @@ def summarize_counters(d: str) -> None:
         rd, wr = fetch_kib * 1024 * f_scale, write_kib * 1024 * w_scale
         need = e["algorithmic_bytes"] + e["scratch_bytes"]
         grid, wg = per["fetch"][k][0][2], per["fetch"][k][0][3]
+        vgpr = int(per["fetch"][k][0][4].get("VGPR_Count", 0))
+        # waves per SIMD the registers allow (512 per lane, allocated in 8s, at most 8 waves)
+        waves = min(8, 512 // max(8, -(-vgpr // 8) * 8)) if vgpr else None
+        elems = e.get("elements", 0)
         row = {"kernel": e["kernel"], "workload": e["workload"], "grid": grid, "workgroup": wg,
                "fetch_kib": round(fetch_kib, 1), "write_kib": round(write_kib, 1), "scaled_bytes": int(rd + wr),
                "algorithmic_bytes": e["algorithmic_bytes"], "scratch_bytes": e["scratch_bytes"],
-               "ratio": round((rd + wr) / need, 4)}
+               "ratio": round((rd + wr) / need, 4), "vgprs": vgpr, "max_waves_per_simd": waves,
+               "bytes_per_element": round((rd + wr) / elems, 3) if elems else None}
         if "lds" in per:
             for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAVES"):
                 row[c] = med("lds", k, c)
         table[e["label"]] = row
-        lines.append(f"| {e['label']} | {e['kernel']} | {grid} / {wg} | {fetch_kib:.1f} | {write_kib:.1f} | "
-                     f"{rd / 1e6:.2f} | {wr / 1e6:.2f} | {e['algorithmic_bytes'] / 1e6:.2f} | "
-                     f"{e['scratch_bytes'] / 1e6:.2f} | {(rd + wr) / need:.3f} | "
+        bpe = f"{row['bytes_per_element']:.2f}" if row["bytes_per_element"] else "-"
+        lines.append(f"| {e['label']} | {e['kernel']} | {grid} / {wg} | {vgpr} ({waves}) | {fetch_kib:.1f} | "
+                     f"{write_kib:.1f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | {e['algorithmic_bytes'] / 1e6:.2f} | "
+                     f"{e['scratch_bytes'] / 1e6:.2f} | {(rd + wr) / need:.3f} | {bpe} | "
                      + (" | ".join(f"{row[c]:.0f}" for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                                                                "SQ_INSTS_LDS")) if "lds" in per else "- | - | -")
                      + " |")
-    print("| Launch | Kernel | Grid / workgroup (threads) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | Read (MB) | "
-          "Written (MB) | Algorithmic (MB) | Scratch (MB) | Moved / (algorithmic + scratch) | "
-          "SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE | SQ_INSTS_LDS |")
-    print("|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    print("| Launch | Kernel | Grid / workgroup (threads) | VGPRs (waves per SIMD) | FETCH_SIZE (KiB) | "
+          "WRITE_SIZE (KiB) | Read (MB) | Written (MB) | Algorithmic (MB) | Scratch (MB) | "
+          "Moved / (algorithmic + scratch) | Moved bytes per element | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE | "
+          "SQ_INSTS_LDS |")
+    print("|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
     print("\n".join(lines))
     print()
     print(f"Calibration: the copy reads and writes {COPY_BYTES} bytes; read bytes = FETCH_SIZE x 1024 x "

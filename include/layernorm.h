@@ -63,8 +63,9 @@ int layernorm_fwd(const void* x, const void* weight, const void* bias, void* y, 
 
 /*
  * Bytes of fp32 workspace layernorm_bwd_rows / layernorm_bwd need for an
- * M x N problem (room for two partial tables of up to min(M, 1024) rows).
- * Pure host arithmetic.  *bytes is written only on RMSNORM_OK.
+ * M x N problem (room for two partial tables of up to min(M, 1024) rows;
+ * min(M, 256) rows for N > RMSNORM_N_MAX).  Pure host arithmetic.  *bytes is
+ * written only on RMSNORM_OK.
  */
 int layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t* bytes);
 

@@ -317,6 +317,7 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
 }
 
 inline int64_t partial_rows_bound(int64_t M) { return std::min(M, kBwdGridMax); }
+inline int64_t wide_partial_rows_bound(int64_t M) { return std::min(M, kComputeUnits); }
 
 // Plan of the wide LayerNorm kernels, for 16-bit rows beyond RMSNORM_N_MAX
 // (up to kLnWideMaxN elements): one 1024-thread workgroup per
@@ -329,7 +330,7 @@ inline RowPlan plan_ln_wide(bool backward, int64_t M, int64_t N, int vec) {
   p.wpr = kMaxBlockWaves;
   p.rpb = 1;
   p.iters = static_cast<int>(ceil_div(N / vec, int64_t(kMaxBlockWaves) * kWave));
-  p.grid = std::max<int64_t>(1, std::min(M, backward ? kComputeUnits : kFwdGridMax));
+  p.grid = std::max<int64_t>(1, std::min(M, backward ? wide_partial_rows_bound(M) : kFwdGridMax));
   p.row_iters = ceil_div(M, p.grid);
   return p;
 }

@@ -18,8 +18,11 @@ int check_dtype_shape(int64_t M, int64_t N, int64_t stride, int dtype) {
   return check_shape(M, N, stride, dtype == RMSNORM_F32 ? RMSNORM_N_MAX : LAYERNORM_N_MAX_16BIT);
 }
 
-// Two partial tables (dw, db) of up to partial_rows_bound(M) rows each.
-int64_t ln_workspace_bytes(int64_t M, int64_t N) { return 2 * partial_rows_bound(M) * N * 4; }
+// Two partial tables (dw, db) of up to partial_rows_bound(M) rows each (rows
+// beyond RMSNORM_N_MAX: the wide backward's grid, at most one workgroup per CU).
+int64_t ln_workspace_bytes(int64_t M, int64_t N) {
+  return 2 * (N > RMSNORM_N_MAX ? wide_partial_rows_bound(M) : partial_rows_bound(M)) * N * 4;
+}
 
 int check_ln_bwd(const void* x, const void* weight, const void* dy, const float* mean, const float* rstd,
                  const void* dx, const float* dw, const float* db, const void* workspace, size_t workspace_bytes,

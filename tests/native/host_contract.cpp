@@ -126,7 +126,7 @@ static void check_wide_plan(const RowPlan& p, bool bwd, int dtype, int64_t M, in
   expect(chunks == p.iters && int64_t(chunks) * 1024 >= nvec, "wide row covered", chunks, nvec);
   expect(chunks * p.vec <= kLnWideColsPerLane, "wide columns per lane", chunks, p.vec);
   expect(p.grid >= 1 && p.grid * row_iters >= M && row_iters == p.row_iters, "wide rows covered", M);
-  expect(!bwd || p.grid <= partial_rows_bound(M), "wide partial rows within the workspace", p.grid);
+  expect(!bwd || p.grid <= wide_partial_rows_bound(M), "wide partial rows within the workspace", p.grid);
   expect(int64_t(N) * 2 < (int64_t(1) << 31) && M * 4 <= (int64_t(1) << 31), "wide descriptor ranges", N, M);
 }
 long g_wide_launches = 0;

@@ -92,7 +92,7 @@ int main(int argc, char** argv) {
             const RowPlan p = plan_ln_wide(bwd, M, N, vec);
             const bool ok = p.vec == vec && p.wpr * kWave == 1024 && p.rpb == 1 && p.iters >= 1 &&
                             int64_t(p.iters) * 1024 * vec >= N && p.iters * vec <= kLnWideColsPerLane &&
-                            p.grid >= 1 && p.grid * p.row_iters >= M && (!bwd || p.grid <= partial_rows_bound(M));
+                            p.grid >= 1 && p.grid * p.row_iters >= M && (!bwd || p.grid <= wide_partial_rows_bound(M));
             if (!ok && bad++ < 10)
               std::printf("bad wide plan: dtype=%d bwd=%d N=%ld vec=%d M=%ld chunks=%d grid=%ld\n", dt, int(bwd),
                           static_cast<long>(N), vec, static_cast<long>(M), p.iters, static_cast<long>(p.grid));

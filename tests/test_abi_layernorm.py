@@ -73,7 +73,8 @@ def test_workspace_query(L):
     assert L.layernorm_bwd_workspace_bytes(17, 16385, F32, ctypes.byref(out)) == E_SHAPE
     assert L.layernorm_bwd_workspace_bytes(17, 32769, F16, ctypes.byref(out)) == E_SHAPE
     assert L.layernorm_bwd_workspace_bytes(300, 32768, BF16, ctypes.byref(out)) == OK
-    assert out.value == 2 * 300 * 32768 * 4
+    assert out.value == 2 * 256 * 32768 * 4  # wide rows: at most one partial row per CU
+    assert L.layernorm_bwd_workspace_bytes(100, 20000, F16, ctypes.byref(out)) == OK and out.value == 2 * 100 * 20000 * 4
     assert L.layernorm_bwd_workspace_bytes(17, 8, 9, ctypes.byref(out)) == E_DTYPE
     assert L.layernorm_bwd_workspace_bytes(17, 8, F32, None) == E_NULL
     assert rn.layernorm_bwd_workspace_bytes(64, 128, 2) == 2 * 64 * 128 * 4
