@@ -766,7 +766,6 @@ def _dispatches(csv_dir: str) -> list:
             d = rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]),
                                                         int(r["Workgroup_Size"]), {}])
             d[3][r["Counter_Name"]] = float(r["Counter_Value"])
-            d[3]["VGPR_Count"] = float(r.get("VGPR_Count") or 0)
     return [(k, *rows[k]) for k in sorted(rows)]
 
 
@@ -806,31 +805,28 @@ def summarize_counters(d: str) -> None:
         rd, wr = fetch_kib * 1024 * f_scale, write_kib * 1024 * w_scale
         need = e["algorithmic_bytes"] + e["scratch_bytes"]
         grid, wg = per["fetch"][k][0][2], per["fetch"][k][0][3]
-        vgpr = int(per["fetch"][k][0][4].get("VGPR_Count", 0))
-        # waves per SIMD the registers allow (512 per lane, allocated in 8s, at most 8 waves)
-        waves = min(8, 512 // max(8, -(-vgpr // 8) * 8)) if vgpr else None
         elems = e.get("elements", 0)
         row = {"kernel": e["kernel"], "workload": e["workload"], "grid": grid, "workgroup": wg,
                "fetch_kib": round(fetch_kib, 1), "write_kib": round(write_kib, 1), "scaled_bytes": int(rd + wr),
                "algorithmic_bytes": e["algorithmic_bytes"], "scratch_bytes": e["scratch_bytes"],
-               "ratio": round((rd + wr) / need, 4), "vgprs": vgpr, "max_waves_per_simd": waves,
+               "ratio": round((rd + wr) / need, 4),
                "bytes_per_element": round((rd + wr) / elems, 3) if elems else None}
         if "lds" in per:
             for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAVES"):
                 row[c] = med("lds", k, c)
         table[e["label"]] = row
         bpe = f"{row['bytes_per_element']:.2f}" if row["bytes_per_element"] else "-"
-        lines.append(f"| {e['label']} | {e['kernel']} | {grid} / {wg} | {vgpr} ({waves}) | {fetch_kib:.1f} | "
+        lines.append(f"| {e['label']} | {e['kernel']} | {grid} / {wg} | {fetch_kib:.1f} | "
                      f"{write_kib:.1f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | {e['algorithmic_bytes'] / 1e6:.2f} | "
                      f"{e['scratch_bytes'] / 1e6:.2f} | {(rd + wr) / need:.3f} | {bpe} | "
                      + (" | ".join(f"{row[c]:.0f}" for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                                                                "SQ_INSTS_LDS")) if "lds" in per else "- | - | -")
                      + " |")
-    print("| Launch | Kernel | Grid / workgroup (threads) | VGPRs (waves per SIMD) | FETCH_SIZE (KiB) | "
+    print("| Launch | Kernel | Grid / workgroup (threads) | FETCH_SIZE (KiB) | "
           "WRITE_SIZE (KiB) | Read (MB) | Written (MB) | Algorithmic (MB) | Scratch (MB) | "
           "Moved / (algorithmic + scratch) | Moved bytes per element | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE | "
           "SQ_INSTS_LDS |")
-    print("|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    print("|---|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
     print("\n".join(lines))
     print()
     print(f"Calibration: the copy reads and writes {COPY_BYTES} bytes; read bytes = FETCH_SIZE x 1024 x "
