@@ -658,7 +658,9 @@ def stream_ceiling():
 
 # ---------------------------------------------------------------------------
 # Counter collection.  `--counter-pass MANIFEST` launches a fixed sequence
-# (COUNTER_CALLS launches of each kernel of each workload, then a plain copy
+# (COUNTER_CALLS launches of each kernel of each workload: the five RMSNorm
+# workloads, every point of the LayerNorm sweep, its unit-test shape, a wide
+# LayerNorm shape, RoPE and SwiGLU; then a plain copy
 # of COPY_BYTES for calibration) under rocprofv3 --pmc, one counter set per
 # run, and writes the sequence to MANIFEST; `--summarize-counters DIR` then
 # attributes the dispatches of DIR/{fetch,write,lds}/*counter_collection.csv
@@ -673,8 +675,8 @@ LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ
 
 def counter_workloads() -> list:
     """(label prefix, kind, workload) of the counter pass, in launch order."""
-    out = [(f"rms {k}", "rms", wl.RMS_WORKLOADS[k]) for k in ("c2", "c3", "c4", "c5")]
-    out += [(f"ln {n}", "ln", wl.ln_sweep(n)) for n in (1024, 4096, 8192)]
+    out = [(f"rms {k}", "rms", wl.RMS_WORKLOADS[k]) for k in ("c1", "c2", "c3", "c4", "c5")]
+    out += [(f"ln {n}", "ln", wl.ln_sweep(n)) for n in wl.LN_SWEEP_NS]
     out.append(("ln unit-test", "ln", wl.LN1))
     out.append(("ln wide", "ln", wl.ln_sweep(8192).scaled(N=32768, name="ln_f16_4096x32768",
                                                              note="16-bit rows beyond 16384 (wide kernels)")))
