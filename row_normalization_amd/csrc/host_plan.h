@@ -238,6 +238,89 @@ constexpr ShapeOverride kShapeOverrides[] = {
 
 // The launch plan of row operation `op` over M rows of N elements of type
 // `dtype`, read in vectors of `vec` elements.
+// Workgroups of about kBlockWaves waves (rpb = kBlockWaves / wpr row groups
+// of wpr waves each), and how many of them fit a CU's kBwdResidentWaves.
+inline int64_t workgroups_per_cu(const RowPlan& p) {
+  int64_t per_cu = 1;
+  while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
+  return per_cu;
+}
+
+// Forward grid: one workgroup per row group, or persistent where a grid of
+// the workgroups that fit the CUs fills every CU with
+// kBwdResidentWaves waves, or with at least kFwdPersistentMinWaves waves
+// whose lanes each carry four 16-byte vectors, and each workgroup then
+// takes at least kFwdPersistentMinSteps row groups (its weights stay in
+// registers across them).  Measured on MI355X: 2-4 % faster at 16384 x 8192
+// and 8192 x 16384, 7-9 % for LayerNorm at 4096 x 8192 and larger; 7-wave
+// rows of four vectors (N = 12800-14336 16-bit, fp32 N = 7168) 0.5-3.6 %
+// faster for RMSNorm and 5-10 % for LayerNorm, which loads two weight
+// vectors per workgroup; for LayerNorm also 6-wave rows of four vectors
+// (12 waves per CU, kLnFwdPersistentMinWaves): 0.7-8 % faster at M = 4096
+// to 16384, N = 10752-12288 and fp32 N = 6144, where RMSNorm's were -3 ...
+// +3 %.  Elsewhere one workgroup per row group is faster: with fewer waves
+// per CU or two vectors per lane a persistent grid keeps too few loads in
+// flight (5-wave rows at N = 5120, 10 waves per CU: 8-12 % slower; 7-wave
+// rows of two vectors at N = 7168: 1-6 % slower), and with 2-4 row groups
+// per workgroup (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a
+// workgroup queue behind each other (3-15 % slower).
+inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int es) {
+  p.rpb = std::max(1, kBlockWaves / p.wpr);
+  const int64_t groups = ceil_div(M, p.rpb);
+  const int64_t per_cu = workgroups_per_cu(p);
+  const int64_t cu_waves = per_cu * p.wpr * p.rpb;
+  const bool four_full_vectors = p.iters == 4 && p.vec * es == 16;
+  const bool persistent =
+      (cu_waves == kBwdResidentWaves ||
+       (cu_waves >= (op == RowOp::kLnFwd ? kLnFwdPersistentMinWaves : kFwdPersistentMinWaves) && four_full_vectors)) &&
+      groups >= kFwdPersistentMinSteps * kComputeUnits * per_cu;
+  p.grid = std::max<int64_t>(1, std::min(groups, persistent ? kComputeUnits * per_cu : kFwdGridMax));
+  p.row_iters = ceil_div(groups, p.grid);
+}
+
+// Backward workgroup shape and grid (the backward is always persistent: each
+// workgroup loops over its rows and writes one partial row per weight), in
+// this order:
+//   1. workgroups of about kBlockWaves waves, as many per CU as fit
+//      kBwdResidentWaves, at most kBwdGridMax of them;
+//   2. where that grid's partial rows exceed kBwdWideShare of the row traffic
+//      and the pipelined row loop is compiled for the plan: one workgroup per
+//      CU, rows of 5-8 waves two to a 16-wave workgroup (bwd_partials_heavy);
+//   3. where the pipelined loop is not compiled: rows of 4-8 waves as one
+//      16-wave workgroup per CU, above kBwdWideShareUnpipelined only;
+//   4. with one workgroup per CU: at least kBwdMinSteps row steps each while
+//      the grid keeps kBwdMinGridWaves waves, then the fewest workgroups that
+//      keep the step count and those waves.
+// Pipelining (bwd_pipelined) and the partial rows' store policy
+// (partials_nontemporal) follow from the resulting plan.
+inline void plan_bwd_grid(RowPlan& p, RowOp op, int64_t M, int es, int dtype) {
+  p.rpb = std::max(1, kBlockWaves / p.wpr);
+  int64_t groups = ceil_div(M, p.rpb);
+  int64_t per_cu = workgroups_per_cu(p);
+  const int64_t default_grid = std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu));
+  const bool fits = bwd_pipeline_fits(op, dtype, p.vec, p.iters);
+  const bool rows_4_to_8 = p.wpr * 2 >= kBlockWaves && p.wpr <= kBlockWaves;
+  const bool rows_5_to_8 = p.wpr * 2 > kBlockWaves && p.wpr <= kBlockWaves;
+  bool sixteen_waves = false;
+  if (fits && bwd_partials_heavy(op, M, es, default_grid)) {
+    sixteen_waves = rows_5_to_8;
+    per_cu = 1;
+  } else if (!fits && rows_4_to_8 && bwd_partials_heavy(op, M, es, default_grid, kBwdWideShareUnpipelined)) {
+    sixteen_waves = true;
+    per_cu = 1;
+  }
+  if (sixteen_waves) {
+    p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
+    groups = ceil_div(M, p.rpb);
+  }
+  p.grid = std::max<int64_t>(1, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)));
+  const bool one_per_cu = p.grid <= kComputeUnits;
+  const int64_t floor_grid = ceil_div(kBwdMinGridWaves, static_cast<int64_t>(p.wpr) * p.rpb);
+  if (one_per_cu) p.grid = std::max<int64_t>(1, std::min(p.grid, std::max(ceil_div(groups, kBwdMinSteps), floor_grid)));
+  p.row_iters = ceil_div(groups, p.grid);
+  if (one_per_cu) p.grid = std::max<int64_t>(1, std::min(p.grid, std::max(ceil_div(groups, p.row_iters), floor_grid)));
+}
+
 inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
   const int es = elsize(dtype);
   RowPlan p{};
@@ -263,56 +346,10 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
       break;
     }
   }
-  p.rpb = std::max(1, kBlockWaves / p.wpr);
-  int64_t groups = ceil_div(M, p.rpb);
-  int64_t per_cu = 1;
-  while (per_cu * 2 * p.wpr * p.rpb <= kBwdResidentWaves) per_cu *= 2;
-  if (backward && bwd_pipeline_fits(op, dtype, p.vec, p.iters) &&
-      bwd_partials_heavy(op, M, es, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)))) {
-    if (p.wpr * 2 > kBlockWaves && p.wpr <= kBlockWaves) {  // rows of 5-8 waves: two per workgroup
-      p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
-      groups = ceil_div(M, p.rpb);
-    }
-    per_cu = 1;
-  } else if (backward && p.wpr * 2 >= kBlockWaves && p.wpr <= kBlockWaves &&
-             bwd_partials_heavy(op, M, es, std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu)),
-                                kBwdWideShareUnpipelined)) {
-    p.rpb = std::max(1, static_cast<int>(kBwdResidentWaves) / p.wpr);
-    groups = ceil_div(M, p.rpb);
-    per_cu = 1;
-  }
-  // The forward is persistent where that grid fills every CU with
-  // kBwdResidentWaves waves, or with at least kFwdPersistentMinWaves waves
-  // whose lanes each carry four 16-byte vectors, and each workgroup then
-  // takes at least kFwdPersistentMinSteps row groups (its weights stay in
-  // registers across them).  Measured on MI355X: 2-4 % faster at 16384 x 8192
-  // and 8192 x 16384, 7-9 % for LayerNorm at 4096 x 8192 and larger; 7-wave
-  // rows of four vectors (N = 12800-14336 16-bit, fp32 N = 7168) 0.5-3.6 %
-  // faster for RMSNorm and 5-10 % for LayerNorm, which loads two weight
-  // vectors per workgroup; for LayerNorm also 6-wave rows of four vectors
-  // (12 waves per CU, kLnFwdPersistentMinWaves): 0.7-8 % faster at M = 4096
-  // to 16384, N = 10752-12288 and fp32 N = 6144, where RMSNorm's were -3 ...
-  // +3 %.  Elsewhere one workgroup per row group is faster: with fewer waves
-  // per CU or two vectors per lane a persistent grid keeps too few loads in
-  // flight (5-wave rows at N = 5120, 10 waves per CU: 8-12 % slower; 7-wave
-  // rows of two vectors at N = 7168: 1-6 % slower), and with 2-4 row groups
-  // per workgroup (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a
-  // workgroup queue behind each other (3-15 % slower).
-  const int64_t cu_waves = per_cu * p.wpr * p.rpb;
-  const bool four_full_vectors = p.iters == 4 && p.vec * es == 16;
-  const bool fwd_persistent =
-      (cu_waves == kBwdResidentWaves ||
-       (cu_waves >= (op == RowOp::kLnFwd ? kLnFwdPersistentMinWaves : kFwdPersistentMinWaves) && four_full_vectors)) &&
-      groups >= kFwdPersistentMinSteps * kComputeUnits * per_cu;
-  const int64_t grid_cap = backward         ? std::min(kBwdGridMax, kComputeUnits * per_cu)
-                           : fwd_persistent ? kComputeUnits * per_cu
-                                            : kFwdGridMax;
-  p.grid = std::max<int64_t>(1, std::min(groups, grid_cap));
-  const bool one_per_cu = backward && p.grid <= kComputeUnits;
-  const int64_t floor_grid = ceil_div(kBwdMinGridWaves, static_cast<int64_t>(p.wpr) * p.rpb);
-  if (one_per_cu) p.grid = std::max<int64_t>(1, std::min(p.grid, std::max(ceil_div(groups, kBwdMinSteps), floor_grid)));
-  p.row_iters = ceil_div(groups, p.grid);
-  if (one_per_cu) p.grid = std::max<int64_t>(1, std::min(p.grid, std::max(ceil_div(groups, p.row_iters), floor_grid)));
+  if (backward)
+    plan_bwd_grid(p, op, M, es, dtype);
+  else
+    plan_fwd_grid(p, op, M, es);
   return p;
 }
 
