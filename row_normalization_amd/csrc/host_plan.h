@@ -363,6 +363,7 @@ inline int64_t wide_partial_rows_bound(int64_t M) { return std::min(M, kComputeU
 // forward takes a row per workgroup.
 inline RowPlan plan_ln_wide(bool backward, int64_t M, int64_t N, int vec) {
   RowPlan p{};
+  p.wide = true;
   p.vec = vec;
   p.wpr = kMaxBlockWaves;
   p.rpb = 1;
@@ -370,6 +371,24 @@ inline RowPlan plan_ln_wide(bool backward, int64_t M, int64_t N, int vec) {
   p.grid = std::max<int64_t>(1, std::min(M, backward ? wide_partial_rows_bound(M) : kFwdGridMax));
   p.row_iters = ceil_div(M, p.grid);
   return p;
+}
+
+// LayerNorm forward of a 16-bit row beyond RMSNORM_N_MAX: the register plan
+// where one exists and its rows span at most kLnWideRegWaves waves (16-byte
+// vectors) or kLnWideRegWavesNarrow (narrower vectors, which the wide kernel
+// reads twice), else the wide kernel.  Measured on MI355X (interleaved
+// comparison, fp16 4096 x N): 16-byte vectors N = 16392 (7 waves) 26 %,
+// 18432 19.5 %, 20480 (8 waves) 18 % faster in the register plan, N = 21504
+// and 23040 (9 waves) 13-17 %, 23552-32768 (10-13 waves) 22-33 % slower;
+// 2- and 4-element vectors N = 16386-16390 (9 waves) 16-21 %, 20482 and
+// 20484 (11 waves) 5-12 % faster.
+constexpr int kLnWideRegWaves = 8;
+constexpr int kLnWideRegWavesNarrow = 11;
+inline RowPlan plan_ln_fwd(int64_t M, int64_t N, int vec, int dtype) {
+  const RowPlan reg = plan_rows(RowOp::kLnFwd, M, N, vec, dtype);
+  if (N <= RMSNORM_N_MAX) return reg;
+  const int max_waves = vec * elsize(dtype) == 16 ? kLnWideRegWaves : kLnWideRegWavesNarrow;
+  return reg.iters > 0 && reg.wpr <= max_waves ? reg : plan_ln_wide(false, M, N, vec);
 }
 
 // Whether a backward workgroup should keep the next row's loads in flight

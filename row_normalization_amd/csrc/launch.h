@@ -26,6 +26,7 @@ struct RowPlan {
   int rpb;        // row groups per block
   int64_t grid;   // workgroups
   int64_t row_iters;
+  bool wide;      // LayerNorm's wide kernels (iters = 1024-vector chunks per row)
   int threads() const { return kWave * wpr * rpb; }
 };
 

@@ -121,8 +121,8 @@ int layernorm_fwd(const void* x, const void* weight, const void* bias, void* y, 
   if (overlap(sy, sm) || overlap(sy, sr) || overlap(sm, sr)) return RMSNORM_E_ALIAS;
 
   const int vec = choose_vec(dtype, N, row_stride, {x, weight, bias, y});
-  const bool wide = N > RMSNORM_N_MAX;  // 16-bit rows only (check_dtype_shape)
-  const RowPlan p = wide ? plan_ln_wide(false, M, N, vec) : plan_rows(RowOp::kLnFwd, M, N, vec, dtype);
+  const RowPlan p = plan_ln_fwd(M, N, vec, dtype);
+  const bool wide = p.wide;
   if (p.iters == 0) return RMSNORM_E_SHAPE;
   LnFwdArgs a{};
   a.x = x;

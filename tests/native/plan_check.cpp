@@ -23,6 +23,12 @@
 
 using namespace rmsn;
 
+static bool in_iters_set(int it) {
+  for (int v : kItersSet)
+    if (v == it) return true;
+  return false;
+}
+
 // With --widths: for every distinct plan (operation, element size, vector
 // width, waves per row, vectors per lane) over N <= RMSNORM_N_MAX, the
 // smallest and the largest N that get it, as lines "rms|ln <element size> N"
@@ -98,6 +104,37 @@ int main(int argc, char** argv) {
                           static_cast<long>(N), vec, static_cast<long>(M), p.iters, static_cast<long>(p.grid));
           }
         }
+  // the LayerNorm forward of those rows: a register plan of at most
+  // kLnWideRegWaves (16-byte vectors) / kLnWideRegWavesNarrow waves, else wide
+  long fwd_reg = 0, fwd_wide = 0;
+  for (int dt = 1; dt < 3; ++dt)
+    for (int64_t N = RMSNORM_N_MAX + 1; N <= LAYERNORM_N_MAX_16BIT; ++N)
+      for (int vec = 1; vec <= 8; vec *= 2) {
+        if (N % vec) continue;
+        for (int64_t M : {int64_t(1), int64_t(4096), int64_t(1) << 20}) {
+          ++n;
+          const RowPlan p = plan_ln_fwd(M, N, vec, dt);
+          bool ok;
+          if (p.wide) {
+            ++fwd_wide;
+            ok = p.vec == vec && p.wpr * kWave == 1024 && p.rpb == 1 && int64_t(p.iters) * 1024 * vec >= N &&
+                 p.iters * vec <= kLnWideColsPerLane && p.grid * p.row_iters >= M;
+          } else {
+            ++fwd_reg;
+            const int max_waves = vec * 2 == 16 ? kLnWideRegWaves : kLnWideRegWavesNarrow;
+            ok = in_iters_set(p.iters) && p.vec * p.iters <= lane_elems_cap(RowOp::kLnFwd, 2) && p.wpr <= max_waves &&
+                 p.threads() <= 1024 && int64_t(p.iters) * kWave * p.wpr * vec >= N &&
+                 p.grid * p.row_iters * p.rpb >= M && (p.wpr == 1 || int64_t(p.wpr - 1) * p.iters * kWave < N / vec);
+          }
+          if (!ok && bad++ < 10)
+            std::printf("bad wide forward plan: dtype=%d N=%ld vec=%d M=%ld wide=%d iters=%d wpr=%d\n", dt,
+                        static_cast<long>(N), vec, static_cast<long>(M), int(p.wide), p.iters, p.wpr);
+        }
+      }
+  if (fwd_reg == 0 || fwd_wide == 0) {
+    ++bad;
+    std::printf("wide forward: %ld register plans, %ld wide plans\n", fwd_reg, fwd_wide);
+  }
   // (element size, N, op, waves per row, vectors per lane), 16-byte vectors
   struct Pin {
     int es;

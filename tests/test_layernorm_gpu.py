@@ -89,11 +89,13 @@ def test_persistent_and_wide_workgroup_shapes(dtype, M, N):
 # 16-bit rows beyond 16384 elements, up to the chapter's 64 KB per row: the
 # wide kernels (one 1024-thread workgroup per row; 16-byte vectors held in
 # registers between the backward's passes, narrower ones read again; 32767
-# takes the most chunks, 32 one-element vectors per lane).  More rows than
-# the backward's 256 workgroups, so they loop; in place and not, split and
-# fused.
+# takes the most chunks, 32 one-element vectors per lane), and for the
+# forward of rows of at most 8 waves (11 with narrower vectors) the register
+# plans (16392: 7 waves x 5 vectors; 20002: 2-element vectors; 20480 at 4100
+# rows: 8 x 5, persistent).  More rows than the backward's 256 workgroups,
+# so they loop; in place and not, split and fused.
 WIDE = [("f16", 300, 16392), ("bf16", 257, 24576), ("f16", 33, 32768), ("bf16", 20, 32767), ("f16", 600, 20002),
-        ("bf16", 5, 16385), ("bf16", 513, 32768)]
+        ("bf16", 5, 16385), ("bf16", 513, 32768), ("f16", 4100, 20480)]
 
 
 @pytest.mark.parametrize("dtype,M,N", WIDE, ids=[f"{d}-{m}x{n}" for d, m, n in WIDE])
