@@ -108,8 +108,11 @@ def test_rmsnorm_gemma_in_place_graph():
     _replay_and_check(graph, reset, outputs, ref)
 
 
-def test_layernorm_fwd_bwd_graph():
-    w = wl.LN1.scaled(M=1500, N=3000)
+@pytest.mark.parametrize("M,N,dtype", [(1500, 3000, "f16"), (300, 20480, "bf16"), (257, 32768, "f16")])
+def test_layernorm_fwd_bwd_graph(M, N, dtype):
+    """Register plans (3000), and 16-bit rows beyond 16384: the forward in a
+    register plan and the wide backward (20480), both wide (32768)."""
+    w = wl.LN1.scaled(M=M, N=N, dtype=dtype)
     _case(w.name, w.M, w.N)
     t = wl.make_inputs(w)
     x, wt, b, dy = (t[k].cuda() for k in ("x", "gamma", "beta", "dy"))
