@@ -353,6 +353,9 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
   return p;
 }
 
+static_assert(kLnWideHeldChunksMin == (RMSNORM_N_MAX + 1 + 8191) / 8192 && kLnWideHeldChunksMax * 8192 == kLnWideMaxN,
+              "the held-row wide backward covers every 16-byte-vector wide row");
+
 inline int64_t partial_rows_bound(int64_t M) { return std::min(M, kBwdGridMax); }
 inline int64_t wide_partial_rows_bound(int64_t M) { return std::min(M, kComputeUnits); }
 

@@ -128,6 +128,15 @@ struct LnBwdArgs {
 // chunk k, so at most kLnWideColsPerLane columns per lane.
 constexpr int kLnWideMaxN = 32768;
 constexpr int kLnWideColsPerLane = kLnWideMaxN / 1024;
+// The wide backward over 16-byte vectors is compiled for rows of
+// kLnWideHeldChunksMin..kLnWideHeldChunksMax chunks (8192 elements each) and
+// keeps the weight row in LDS, chunks * 16 KB of it: within gfx950's 160 KB
+// of LDS per workgroup (kLdsPerWorkgroup), beside its 256-byte sum table.
+constexpr int kLdsPerWorkgroup = 160 * 1024;
+constexpr int kLnWideHeldChunksMin = 3;  // rows beyond the register plans' 16384 elements
+constexpr int kLnWideHeldChunksMax = kLnWideMaxN / 8192;
+constexpr int kLnWideHeldLdsBytes(int chunks) { return chunks * 1024 * 16; }
+static_assert(kLnWideHeldLdsBytes(kLnWideHeldChunksMax) + 256 <= kLdsPerWorkgroup, "weight row fits LDS");
 
 // RoPE: one work item = one token, one group of kRopeGroup heads, one VEC
 // vector of the half-head (and the matching vector of the other half).

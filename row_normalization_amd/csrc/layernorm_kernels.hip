@@ -499,20 +499,148 @@ __global__ __launch_bounds__(kWideThreads) void layernorm_fwd_wide_kernel(const 
   }
 }
 
-// Backward: per row, the two row sums (pass 1), then dx and the dw / db
-// contributions (pass 2).  x and dy stay in registers between the passes for
-// 16-byte vectors; narrower vectors (N not a multiple of 8, or misaligned
-// rows) would need more registers than a lane of a 1024-thread workgroup
-// has, so pass 2 reads them again, from L2 (pass 1 loads them with the
-// allocating policy).  The weight is read per pass from the
-// caches.  dw and db partials stay in fp32 registers across the workgroup's
-// rows; the workgroup writes one partial row of each.
+// A value every lane of the workgroup holds alike, moved to a scalar register.
+__device__ __forceinline__ float uniform_f32(uint32_t bits) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(bits));
+}
+
+// Backward over rows read in 16-byte vectors: per row, the two row sums
+// (pass 1), then dx and the dw / db contributions (pass 2), with the
+// workgroup's next row on its way during pass 2.  Rows of CH chunks (3 or 4:
+// 16385-32768 elements).  x and dy of a row stay in registers between the
+// passes; dw and db partials stay in fp32 registers across the workgroup's
+// rows (one partial row of each at the end).  The weight is copied into LDS
+// once per workgroup (CH * 16 KB; gfx950 gives a workgroup up to 160 KB) and
+// read from there, so no load of pass 2 queues behind the next row's loads,
+// which the vector-memory counter retires in issue order.  As soon as pass 2
+// has used chunk k of the row (dx stored, dw and db added), it loads chunk k
+// of the next row into the same registers: one register set, which is what
+// fits a lane of a 1024-thread workgroup (128 registers; two full sets would
+// not).  Offsets at or past a row's bytes -- the unfilled end of the last
+// chunk, and every offset once the workgroup has no next row -- read zero
+// and store nothing through the row descriptors.
+template <typename S, int CH>
+__global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_held_kernel(const LnBwdArgs a) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(S));
+  typedef Pack<S, VEC> P;
+  const Lane L(kWideThreads / kWave);
+  __shared__ float red[2][2][kMaxBlockWaves];
+  extern __shared__ u32x4_t wlds[];  // CH * kWideThreads weight vectors, zero past the row
+  const int64_t steps = a.row_iters;
+  const uint32_t t = threadIdx.x;
+  const uint32_t voff = t * 16u;
+  constexpr uint32_t kChunkBytes = kWideThreads * 16u;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.N) * sizeof(S);
+  const Rsrc rw = make_rsrc(a.weight, row_bytes);
+  const Rsrc rmean = make_rsrc(a.mean, static_cast<uint32_t>(a.M) * 4u);
+  const Rsrc rrstd = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
+#pragma unroll
+  for (int k = 0; k < CH; ++k)
+    wlds[k * kWideThreads + t] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff + k * kChunkBytes, 0, kDefault);
+  float accw[CH][VEC], accb[CH][VEC];
+#pragma unroll
+  for (int k = 0; k < CH; ++k)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) accw[k][e] = accb[k][e] = 0.f;
+
+  // the first row (grid <= M, so every workgroup has one)
+  int64_t row = blockIdx.x;
+  bool active = row < a.M;
+  Rsrc rx = make_rsrc(static_cast<const S*>(a.x) + (active ? row * a.stride : 0), active ? row_bytes : 0u);
+  Rsrc rd = make_rsrc(static_cast<const S*>(a.dy) + (active ? row * a.stride : 0), active ? row_bytes : 0u);
+  const uint32_t soff = active ? static_cast<uint32_t>(row) * 4u : kOutOfRange;
+  float mean = uniform_f32(__builtin_amdgcn_raw_buffer_load_b32(rmean, soff, 0, kDefault));
+  float rstd = uniform_f32(__builtin_amdgcn_raw_buffer_load_b32(rrstd, soff, 0, kDefault));
+  P xv[CH], dv[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    xv[k] = buf_load<S, VEC, kLnLoadXdy>(rx, voff + k * kChunkBytes);
+    dv[k] = buf_load<S, VEC, kLnLoadXdy>(rd, voff + k * kChunkBytes);
+  }
+  __syncthreads();  // the weight is in LDS
+
+  for (int64_t step = 0; step < steps; ++step) {
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const P w = __builtin_bit_cast(P, wlds[k * kWideThreads + t]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float xh = (xv[k].get(e) - mean) * rstd;
+        const float g = w.get(e) * dv[k].get(e);
+        s1 = fmaf(xh, g, s1);
+        s2 += g;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      xv[k].keep_packed();
+      dv[k].keep_packed();
+    }
+    block_sum2(s1, s2, red, step, L);
+    const float c1 = uniform_f32(__builtin_bit_cast(uint32_t, s1 * a.inv_n));
+    const float c2 = uniform_f32(__builtin_bit_cast(uint32_t, s2 * a.inv_n));
+
+    const Rsrc rdx = make_rsrc(static_cast<S*>(a.dx) + (active ? row * a.stride : 0), active ? row_bytes : 0u);
+    const int64_t nrow = row + gridDim.x;
+    const bool nactive = step + 1 < steps && nrow < a.M;
+    const Rsrc nrx = make_rsrc(static_cast<const S*>(a.x) + (nactive ? nrow * a.stride : 0), nactive ? row_bytes : 0u);
+    const Rsrc nrd = make_rsrc(static_cast<const S*>(a.dy) + (nactive ? nrow * a.stride : 0), nactive ? row_bytes : 0u);
+    const uint32_t nsoff = nactive ? static_cast<uint32_t>(nrow) * 4u : kOutOfRange;
+    const float nmean = uniform_f32(__builtin_amdgcn_raw_buffer_load_b32(rmean, nsoff, 0, kDefault));
+    const float nrstd = uniform_f32(__builtin_amdgcn_raw_buffer_load_b32(rrstd, nsoff, 0, kDefault));
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const uint32_t o = voff + k * kChunkBytes;
+      const P w = __builtin_bit_cast(P, wlds[k * kWideThreads + t]);
+      float out[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float df = dv[k].get(e);
+        const float xh = (xv[k].get(e) - mean) * rstd;
+        out[e] = (w.get(e) * df - fmaf(xh, c1, c2)) * rstd;
+        accw[k][e] = fmaf(df, xh, accw[k][e]);
+        accb[k][e] += df;
+      }
+      buf_store<S, VEC, kLnStoreDx>(round_pack<S, VEC>(out), rdx, o);
+      // chunk k's arithmetic stays ahead of the loads that reuse its
+      // registers (else the scheduler defers the dw sums and spills)
+      __builtin_amdgcn_sched_barrier(0);
+      // rows never overlap, so the next row's dy is not this row's dx
+      xv[k] = buf_load<S, VEC, kLnLoadXdy>(nrx, o);
+      dv[k] = buf_load<S, VEC, kLnLoadXdy>(nrd, o);
+    }
+    row = nrow;
+    active = nactive;
+    mean = nmean;
+    rstd = nrstd;
+  }
+  const Rsrc rpw = make_rsrc(a.partials + static_cast<int64_t>(blockIdx.x) * a.N, static_cast<uint32_t>(a.N) * 4u);
+  const Rsrc rpb =
+      make_rsrc(a.partials + (static_cast<int64_t>(gridDim.x) + blockIdx.x) * a.N, static_cast<uint32_t>(a.N) * 4u);
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const uint32_t o = (k * kWideThreads + t) * VEC * 4u;
+    if (a.partials_nt) {
+      buf_store_f32<VEC, kNontemporal>(accw[k], rpw, o);
+      buf_store_f32<VEC, kNontemporal>(accb[k], rpb, o);
+    } else {
+      buf_store_f32<VEC, kDefault>(accw[k], rpw, o);
+      buf_store_f32<VEC, kDefault>(accb[k], rpb, o);
+    }
+  }
+}
+
+// Backward over rows read in narrower vectors (N not a multiple of 8, or
+// misaligned rows): a row in such vectors would need more registers than a
+// lane of a 1024-thread workgroup has, so pass 2 reads x and dy again, from
+// L2 (pass 1 loads them with the allocating policy), and the weight is read
+// per pass from the caches.  One row at a time; dw and db partials as above.
 template <typename S, int VEC>
 __global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_kernel(const LnBwdArgs a) {
   constexpr int KMAX = kLnWideColsPerLane / VEC;
-  constexpr bool kHold = VEC * sizeof(S) == 16;
-  constexpr int kPass1 = kHold ? kLnLoadXdy : kDefault;
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
+  static_assert(kPack < 16, "16-byte vectors take the held-row kernel");
   const Lane L(kWideThreads / kWave);
   __shared__ float red[2][2][kMaxBlockWaves];
   const int chunks = a.chunks;
@@ -540,13 +668,12 @@ __global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_kernel(const 
     const float mean = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rmean, soff, 0, kDefault));
     const float rstd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrstd, soff, 0, kDefault));
 
-    Pack<S, VEC> xv[kHold ? KMAX : 1], dv[kHold ? KMAX : 1];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const uint32_t o = k < chunks ? voff + k * kChunkBytes : kOutOfRange;
-      const Pack<S, VEC> x = buf_load<S, VEC, kPass1>(rx, o);
-      const Pack<S, VEC> dy = buf_load<S, VEC, kPass1>(rd, o);
+      const Pack<S, VEC> x = buf_load<S, VEC, kDefault>(rx, o);
+      const Pack<S, VEC> dy = buf_load<S, VEC, kDefault>(rd, o);
       const Pack<S, VEC> w = buf_load<S, VEC, kDefault>(rw, o);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -554,17 +681,6 @@ __global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_kernel(const 
         const float g = w.get(e) * dy.get(e);
         s1 = fmaf(xh, g, s1);
         s2 += g;
-      }
-      if constexpr (kHold) {
-        xv[k] = x;
-        dv[k] = dy;
-      }
-    }
-    if constexpr (kHold) {
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        xv[k].keep_packed();
-        dv[k].keep_packed();
       }
     }
     block_sum2(s1, s2, red, step, L);
@@ -574,16 +690,10 @@ __global__ __launch_bounds__(kWideThreads) void layernorm_bwd_wide_kernel(const 
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const uint32_t o = k < chunks ? voff + k * kChunkBytes : kOutOfRange;
-      Pack<S, VEC> x, dy;
-      if constexpr (kHold) {
-        x = xv[k];
-        dy = dv[k];
-      } else {
-        // every element of dy this lane reads here it has not yet overwritten
-        // (dx may be dy itself: this lane stores only the elements it loads)
-        x = buf_load<S, VEC, kLnLoadXdy>(rx, o);
-        dy = buf_load<S, VEC, kLnLoadXdy>(rd, o);
-      }
+      // every element of dy this lane reads here it has not yet overwritten
+      // (dx may be dy itself: this lane stores only the elements it loads)
+      const Pack<S, VEC> x = buf_load<S, VEC, kLnLoadXdy>(rx, o);
+      const Pack<S, VEC> dy = buf_load<S, VEC, kLnLoadXdy>(rd, o);
       const Pack<S, VEC> w = buf_load<S, VEC, kDefault>(rw, o);
       float out[VEC];
 #pragma unroll
@@ -671,7 +781,18 @@ hipError_t ln_wide_bwd_s(const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
     case 1: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 2>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((layernorm_bwd_wide_kernel<S, 8>), grid, block, 0, s, a); break;
+    case 8:
+      // 16385-32768 elements: three or four 8192-element chunks
+      static_assert(kLnWideHeldChunksMin == 3 && kLnWideHeldChunksMax == 4, "held-row instantiations");
+      static_assert(kWideThreads * 16 == 16384, "a chunk of 16-byte vectors");
+      if (a.chunks == 3) {
+        hipLaunchKernelGGL((layernorm_bwd_wide_held_kernel<S, 3>), grid, block, kLnWideHeldLdsBytes(3), s, a);
+      } else if (a.chunks == 4) {
+        hipLaunchKernelGGL((layernorm_bwd_wide_held_kernel<S, 4>), grid, block, kLnWideHeldLdsBytes(4), s, a);
+      } else {
+        return hipErrorInvalidValue;  // never planned
+      }
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

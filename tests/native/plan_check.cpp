@@ -7,7 +7,8 @@
 // the planner picks for a few widths where the ordering of its rules
 // matters.  For 16-bit LayerNorm rows beyond RMSNORM_N_MAX (up to
 // LAYERNORM_N_MAX_16BIT) it checks that the wide plan covers the row within
-// the wide kernels' registers.  Built and
+// the wide kernels' registers, and that the backward over 16-byte vectors
+// gets a chunk count its held-row kernel is compiled for.  Built and
 // run by tests/test_plan.py; prints one summary line and exits non-zero on
 // failure.
 #include <cstdio>
@@ -98,7 +99,11 @@ int main(int argc, char** argv) {
             const RowPlan p = plan_ln_wide(bwd, M, N, vec);
             const bool ok = p.vec == vec && p.wpr * kWave == 1024 && p.rpb == 1 && p.iters >= 1 &&
                             int64_t(p.iters) * 1024 * vec >= N && p.iters * vec <= kLnWideColsPerLane &&
-                            p.grid >= 1 && p.grid * p.row_iters >= M && (!bwd || p.grid <= wide_partial_rows_bound(M));
+                            p.grid >= 1 && p.grid * p.row_iters >= M && (!bwd || p.grid <= wide_partial_rows_bound(M)) &&
+                            // the backward over 16-byte vectors: a compiled held-row chunk count
+                            (!bwd || vec * 2 != 16 ||
+                             (p.iters >= kLnWideHeldChunksMin && p.iters <= kLnWideHeldChunksMax &&
+                              kLnWideHeldLdsBytes(p.iters) + 256 <= kLdsPerWorkgroup));
             if (!ok && bad++ < 10)
               std::printf("bad wide plan: dtype=%d bwd=%d N=%ld vec=%d M=%ld chunks=%d grid=%ld\n", dt, int(bwd),
                           static_cast<long>(N), vec, static_cast<long>(M), p.iters, static_cast<long>(p.grid));
