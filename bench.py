@@ -714,8 +714,10 @@ def counter_pass(manifest: str) -> None:
             path.bwd_rows()  # the partial-row count, before the counted launches
             torch.cuda.synchronize()
             part = 2 * path.partial_rows * w.N * 4
-            launch(f"{prefix} bwd_rows", "layernorm_bwd_wide_kernel" if wide else "layernorm_bwd_rows_kernel",
-                   path.bwd_rows, b["bwd_rows"], part, w.name, w.M * w.N)
+            # wide rows in 16-byte vectors (dense, N a multiple of 8) take the held-row kernel
+            bwd_kernel = ("layernorm_bwd_wide_held_kernel" if w.N % 8 == 0 else "layernorm_bwd_wide_kernel") if wide \
+                else "layernorm_bwd_rows_kernel"
+            launch(f"{prefix} bwd_rows", bwd_kernel, path.bwd_rows, b["bwd_rows"], part, w.name, w.M * w.N)
             launch(f"{prefix} reduce", "rmsnorm_dgamma_reduce_kernel", path.reduce, 8 * w.N, part, w.name)
         del path
         torch.cuda.empty_cache()
