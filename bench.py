@@ -320,41 +320,61 @@ SAMPLES = 50
 CALLS = 20
 
 
+def _ln_point(w, samples: int) -> dict:
+    """Forward, row pass, column sum and the dependent backward pair of one
+    LayerNorm workload, each the median over `samples` samples."""
+    path = LnPath(w)
+    path.step()
+    t_f, t_r, t_d = (time_calls(fn, samples)["median_s"] for fn in (path.fwd, path.bwd_rows, path.reduce))
+    t_b = time_calls(path.bwd, samples)["median_s"]
+    b = wl.ln_algorithmic_bytes(w.M, w.N, w.elsize)
+    numel_bytes = w.M * w.N * w.elsize
+    point = {
+        "N": w.N,
+        "fwd_us": round(t_f * 1e6, 2), "bwd_rows_us": round(t_r * 1e6, 2), "reduce_us": round(t_d * 1e6, 2),
+        "bwd_us": round(t_b * 1e6, 2),
+        "fwd_gbps_page_formula": round(2 * numel_bytes / t_f / 1e9, 1),
+        "bwd_gbps_page_formula": round(3 * numel_bytes / t_b / 1e9, 1),
+        "fwd_frac": round(b["fwd"] / t_f / 1e9 / PEAK_HBM_GBPS, 4),
+        "bwd_rows_frac": round(b["bwd_rows"] / t_r / 1e9 / PEAK_HBM_GBPS, 4),
+        "bwd_frac": round(b["bwd"] / t_b / 1e9 / PEAK_HBM_GBPS, 4),
+        # the backward's two launches timed apart and added (no dependent pair)
+        "bwd_parts_frac": round(b["bwd"] / (t_r + t_d) / 1e9 / PEAK_HBM_GBPS, 4),
+        "partial_rows": path.partial_rows,
+    }
+    del path
+    torch.cuda.empty_cache()
+    return point
+
+
 def layernorm_sweep(samples: int, ns=None) -> dict:
-    """The LayerNorm chapter's sweep: M = 4096 fp16, N = 512 * i, i = 2 .. 31."""
+    """The LayerNorm chapter's sweep: M = 4096 fp16, N = 512 * i, i = 2 .. 31;
+    beside it, outside the medians, rows beyond 16384 elements up to the
+    chapter's 64 KB (the wide kernels)."""
     points = []
     for N in (ns or wl.LN_SWEEP_NS):
-        w = wl.ln_sweep(N)
-        path = LnPath(w)
-        path.step()
-        t_f, t_r, t_d = (time_calls(fn, samples)["median_s"] for fn in (path.fwd, path.bwd_rows, path.reduce))
-        t_b = time_calls(path.bwd, samples)["median_s"]
-        b = wl.ln_algorithmic_bytes(w.M, w.N, w.elsize)
-        numel_bytes = w.M * w.N * w.elsize
-        points.append({
-            "N": N,
-            "fwd_us": round(t_f * 1e6, 2), "bwd_rows_us": round(t_r * 1e6, 2), "reduce_us": round(t_d * 1e6, 2),
-            "bwd_us": round(t_b * 1e6, 2),
-            "fwd_gbps_page_formula": round(2 * numel_bytes / t_f / 1e9, 1),
-            "bwd_gbps_page_formula": round(3 * numel_bytes / t_b / 1e9, 1),
-            "fwd_frac": round(b["fwd"] / t_f / 1e9 / PEAK_HBM_GBPS, 4),
-            "bwd_rows_frac": round(b["bwd_rows"] / t_r / 1e9 / PEAK_HBM_GBPS, 4),
-            "bwd_frac": round(b["bwd"] / t_b / 1e9 / PEAK_HBM_GBPS, 4),
-            # the backward's two launches timed apart and added (no dependent pair)
-            "bwd_parts_frac": round(b["bwd"] / (t_r + t_d) / 1e9 / PEAK_HBM_GBPS, 4),
-            "partial_rows": path.partial_rows,
-        })
+        points.append(_ln_point(wl.ln_sweep(N), samples))
         print(f"[layernorm sweep] N={N}: fwd {points[-1]['fwd_us']} us, bwd {points[-1]['bwd_us']} us",
               file=sys.stderr, flush=True)
-        del path
-        torch.cuda.empty_cache()
+    wide = []
+    for N in (() if ns else LN_WIDE_NS):
+        wide.append(_ln_point(wl.ln_sweep(8192).scaled(N=N, name=f"ln_f16_4096x{N}"), samples))
+        print(f"[layernorm wide] N={N}: fwd {wide[-1]['fwd_us']} us, bwd {wide[-1]['bwd_us']} us",
+              file=sys.stderr, flush=True)
     med = lambda key: float(np.median([p[key] for p in points]))
     return {"workload": f"layernorm fp16 M={wl.LN_SWEEP_M}, N = 512*i for i = 2..31",
             "protocol": f"median of {samples} samples x {CALLS} back-to-back calls; bwd: row pass and column sum "
                         "as one dependent pair per call; bwd_parts: the two timed apart, added",
             "median_fwd_frac": round(med("fwd_frac"), 4), "median_bwd_frac": round(med("bwd_frac"), 4),
             "median_bwd_parts_frac": round(med("bwd_parts_frac"), 4),
-            "median_bwd_gbps_page_formula": round(med("bwd_gbps_page_formula"), 1), "points": points}
+            "median_bwd_gbps_page_formula": round(med("bwd_gbps_page_formula"), 1), "points": points,
+            "wide": {"workload": f"layernorm fp16 M={wl.LN_SWEEP_M}, rows beyond 16384 elements (wide kernels), "
+                                 "not in the medians", "points": wide}}
+
+
+# Wide LayerNorm rows timed beside the sweep: 3 chunks with one vector in the
+# last, 3 full chunks, 4 full chunks (the chapter's 64 KB rows).
+LN_WIDE_NS = (16392, 24576, 32768)
 
 
 # Untimed work before each measurement.  On MI355X a new stream of launches
@@ -950,6 +970,10 @@ def main():
         c["traffic_bytes"] = {leg: traffic_tab.get(f"rms {k} {leg}") for leg in ("fwd", "bwd_rows", "reduce")}
     for pt in (out["layernorm"] or {}).get("points", []):
         pt["traffic_bytes"] = {leg: traffic_tab.get(f"ln {pt['N']} {leg}") for leg in ("fwd", "bwd_rows", "reduce")}
+    for pt in (out["layernorm"] or {}).get("wide", {}).get("points", []):
+        # the counter pass covers the 4096 x 32768 wide shape
+        pt["traffic_bytes"] = {leg: traffic_tab.get(f"ln wide {leg}") if pt["N"] == 32768 else None
+                               for leg in ("fwd", "bwd_rows", "reduce")}
     if args.no_elementwise:
         out["rope"] = out["swiglu"] = None
     else:
