@@ -93,7 +93,10 @@ def test_persistent_and_wide_workgroup_shapes(dtype, M, N):
 # forward of rows of at most 8 waves (11 with narrower vectors) the register
 # plans (16392: 7 waves x 5 vectors; 20002: 2-element vectors; 20480 at 4100
 # rows: 8 x 5, persistent).  More rows than the backward's 256 workgroups,
-# so they loop; in place and not, split and fused.
+# so they loop; in place and not, split and fused.  The backward over 16-byte
+# vectors loads each workgroup's next row during a row's second pass: three
+# chunks with a ragged last step (300, 257 and 4100 rows: 44, 1 and 4 rows
+# in it), four chunks over three steps (513 rows) and in one (33).
 WIDE = [("f16", 300, 16392), ("bf16", 257, 24576), ("f16", 33, 32768), ("bf16", 20, 32767), ("f16", 600, 20002),
         ("bf16", 5, 16385), ("bf16", 513, 32768), ("f16", 4100, 20480)]
 
