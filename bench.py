@@ -651,12 +651,15 @@ def cpu_baseline(w: wl.Workload, seconds: float, all_cores_seconds: float) -> di
 
 
 CEILING_PROBE = os.path.join(ROOT, "tests", "native", "bin", "stream_ceiling")
+CEILING_MIXES = ("read", "read1_write1", "read2_write1", "read2_write1_in_place")
 
 
 def stream_ceiling():
     """GB/s of plain streaming kernels (16-byte nontemporal vectors, 256 MiB per
     operand) for the read/write mixes of the row kernels: read only, one read
-    per write, two reads per write (tests/native/stream_ceiling.hip).  Run as a
+    per write, two reads per write, and two reads per write in place (dx over
+    dy), each the best over grid-stride and row-walk shapes, both cache
+    policies (tests/native/stream_ceiling.hip).  Run as a
     child process before this process touches the GPU.  None if the probe has
     not been built."""
     import subprocess
@@ -670,9 +673,11 @@ def stream_ceiling():
         return None
     res = json.loads(r.stdout.strip().splitlines()[-1])
     print(f"[ceiling] {res}", file=sys.stderr, flush=True)
-    # the JSON line keeps the best shape of each mix; the probe itself lists all
-    for mix in ("read", "read1_write1", "read2_write1"):
-        res[mix].pop("hot_gbps_by_shape", None)
+    # the JSON line keeps the three fastest shapes of each mix; the probe itself lists all
+    for mix in CEILING_MIXES:
+        shapes = res[mix].pop("hot_gbps_by_shape", {})
+        res[mix]["top_hot_shapes"] = dict(sorted(shapes.items(), key=lambda kv: -kv[1])[:3])
+        res[mix]["shapes_timed"] = len(shapes)
     return res
 
 
@@ -957,7 +962,9 @@ def main():
         "stream_ceiling": ceiling,
         "kernels_vs_ceiling": None if not ceiling else {
             "fwd": round(b["fwd"] / kern["fwd"]["median_s"] / 1e9 / ceiling["read1_write1"]["hot_gbps"], 4),
-            "bwd_rows": round(achieved / ceiling["read2_write1"]["hot_gbps"], 4)},
+            "bwd_rows": round(achieved / ceiling["read2_write1"]["hot_gbps"], 4),
+            "bwd_rows_vs_in_place": (round(achieved / ceiling["read2_write1_in_place"]["hot_gbps"], 4)
+                                     if "read2_write1_in_place" in ceiling else None)},
     }
     del overlapped, path, schedules
     torch.cuda.empty_cache()

@@ -143,31 +143,38 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
   return found;
 }
 
-// Backward grids where the weight-gradient partial rows are a heavy share of
-// the traffic.  Each backward workgroup writes one fp32 partial row per
-// weight (two for LayerNorm) after its last row step, which the column sum
-// reads back: with `grid` workgroups, tables * grid * 4 bytes per column
-// against 3 * M * es of row traffic.  Where that share exceeds kBwdWideShare
-// (and the pipelined row loop is compiled for the plan: a workgroup alone on
-// its CU needs it to keep loads in flight through its barriers), the
-// backward runs one workgroup per CU instead of two:
-//   * rows of 5-8 waves as workgroups of two row groups (16 waves);
-//   * other rows keep their workgroup shape, one per CU;
-//   * each workgroup takes at least kBwdMinSteps row steps while the grid
-//     keeps kBwdMinGridWaves waves (8 per CU), and the grid is then the
-//     fewest workgroups that keep the step count and those waves.
-// Measured on MI355X (interleaved comparison; full backward = row pass and
-// column sum): LayerNorm fp16 at M = 4096, N = 1024-5120, 4-17 % faster
-// (N = 1024 17 %, 2048 15 %, 4096 16 %), the chapter's 1151 x 8192 17 %,
-// 8192 x 2048 12 %, fp32 4096 x 2048 10 %; RMSNorm bf16 4096 x 4096 10 %,
-// 4096 x 3072 13 %, 8192 x 2048 6.5 %, 1151 x 8192 9 %, 700 x 16384 7 %.
-// Shapes below the share (16384 x 8192, 32768 x 5120, 16384 x 1024) are
-// unchanged: there two workgroups of the row shape per CU were faster (the
-// 16-wave shape 2-4 % slower at 16384 x 8192 and 32768 x 5120).  Rows of 1-4
-// waves in 16-wave workgroups (4-16 row groups to combine) were 3-37 %
-// slower, so they keep their shape; one workgroup per CU of fewer than
-// kBwdMinGridWaves / 256 waves was slower (4096 x 1024 with 128 workgroups
-// of 8 waves: 13 %).
+// Backward grids.  Where the pipelined row loop is compiled for the plan
+// (a workgroup alone on its CU needs it to keep loads in flight through its
+// barriers), the backward runs one workgroup per CU, of the row's own shape
+// (about kBlockWaves waves), pipelined.  Measured on MI355X (interleaved
+// comparison, full backward = row pass and column sum) against two
+// workgroups per CU without the pipeline: RMSNorm bf16 16384 x 8192 (Gemma,
+// in place) 2.2 % faster (the fwd + bwd step 1.5 %), 32768 x 5120 2.1 %,
+// 16384 x 1024-6144 2.8-5.0 %, 32768 x 1024-8192 1.2-3.3 %, 65536 x 4096
+// 1.1 %; fp32 8192 x 1024-4096 1.7-3.5 %, 16384 x 1024-4096 0.2-1.3 %;
+// LayerNorm fp16 32768 x 1024-8192 2.2-4.6 % (6144: 0.8 % slower), fp32
+// 16384 x 2048 and 4096 1.9 and 2.5 %.  (Two workgroups per CU also write
+// twice the partial rows.)
+// Each workgroup writes one fp32 partial row per weight (two for LayerNorm)
+// after its last row step, which the column sum reads back: with `grid`
+// workgroups, tables * grid * 4 bytes per column against 3 * M * es of row
+// traffic.  Where that share exceeds kBwdWideShare, rows of 5-8 waves run
+// two to a 16-wave workgroup (still one per CU): 5-7 waves alone on a CU keep
+// too few loads in flight (LayerNorm fp16 4096 x 4608-6656 3-18 % slower,
+// 8192 x 6144 10 %, RMSNorm bf16 2048 x 8192 6 % slower as one 8-wave
+// workgroup).  With one workgroup per CU each takes at least kBwdMinSteps
+// row steps while the grid keeps kBwdMinGridWaves waves (8 per CU), and the
+// grid is then the fewest workgroups that keep the step count and those
+// waves.
+// Measured on MI355X against two workgroups per CU (interleaved comparison;
+// full backward) where the partial rows weigh: LayerNorm fp16 at M = 4096,
+// N = 1024-5120, 4-17 % faster (N = 1024 17 %, 2048 15 %, 4096 16 %), the
+// chapter's 1151 x 8192 17 %, 8192 x 2048 12 %, fp32 4096 x 2048 10 %;
+// RMSNorm bf16 4096 x 4096 10 %, 4096 x 3072 13 %, 8192 x 2048 6.5 %,
+// 1151 x 8192 9 %, 700 x 16384 7 %.  Rows of 1-4 waves in 16-wave
+// workgroups (4-16 row groups to combine) were 3-37 % slower, so they keep
+// their shape; one workgroup per CU of fewer than kBwdMinGridWaves / 256
+// waves was slower (4096 x 1024 with 128 workgroups of 8 waves: 13 %).
 constexpr double kBwdWideShare = 0.03;
 // Where the pipelined loop is not compiled for the plan (bf16 LayerNorm, whose
 // unpacking needs more registers; narrower vectors), only rows of 4-8 waves
@@ -283,9 +290,10 @@ inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int es) {
 // this order:
 //   1. workgroups of about kBlockWaves waves, as many per CU as fit
 //      kBwdResidentWaves, at most kBwdGridMax of them;
-//   2. where that grid's partial rows exceed kBwdWideShare of the row traffic
-//      and the pipelined row loop is compiled for the plan: one workgroup per
-//      CU, rows of 5-8 waves two to a 16-wave workgroup (bwd_partials_heavy);
+//   2. where the pipelined row loop is compiled for the plan: one workgroup
+//      per CU; where the partial rows of the grid of step 1 exceed
+//      kBwdWideShare of the row traffic, rows of 5-8 waves two to a 16-wave
+//      workgroup (bwd_partials_heavy);
 //   3. where the pipelined loop is not compiled: rows of 4-8 waves as one
 //      16-wave workgroup per CU, above kBwdWideShareUnpipelined only;
 //   4. with one workgroup per CU: at least kBwdMinSteps row steps each while
@@ -302,8 +310,8 @@ inline void plan_bwd_grid(RowPlan& p, RowOp op, int64_t M, int es, int dtype) {
   const bool rows_4_to_8 = p.wpr * 2 >= kBlockWaves && p.wpr <= kBlockWaves;
   const bool rows_5_to_8 = p.wpr * 2 > kBlockWaves && p.wpr <= kBlockWaves;
   bool sixteen_waves = false;
-  if (fits && bwd_partials_heavy(op, M, es, default_grid)) {
-    sixteen_waves = rows_5_to_8;
+  if (fits) {
+    sixteen_waves = rows_5_to_8 && bwd_partials_heavy(op, M, es, default_grid);
     per_cu = 1;
   } else if (!fits && rows_4_to_8 && bwd_partials_heavy(op, M, es, default_grid, kBwdWideShareUnpipelined)) {
     sixteen_waves = true;
@@ -401,7 +409,8 @@ inline RowPlan plan_ln_fwd(int64_t M, int64_t N, int vec, int dtype) {
 // MI355X (bf16): 8192 x 16384, 8192 x 15872, 16384 x 15360 and 16384 x 9216
 // row passes 5-9 % faster pipelined; one 8-wave workgroup per CU at LayerNorm
 // fp16 4096 x 2048 16 % faster pipelined than not; with two workgroups per
-// CU (16384 x 8192, 32768 x 5120) pipelining was 2-8 % slower.
+// CU (16384 x 8192, 32768 x 5120) pipelining was 2-8 % slower.  (The planner
+// gives two workgroups per CU only where the pipelined loop is not compiled.)
 inline bool bwd_pipelined(RowOp op, const RowPlan& p, int dtype) {
   const bool alone_on_cu = p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits;
   return alone_on_cu && bwd_pipeline_fits(op, dtype, p.vec, p.iters);

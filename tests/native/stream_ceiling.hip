@@ -1,13 +1,22 @@
 // What plain streaming kernels reach on this GPU for the read/write mixes of
 // the row kernels, as the reference point for their HBM rooflines: read only,
-// one read per write (the forwards: x in, y out) and two reads per write (the
-// backwards: x and dy in, dx out).  256 MiB per operand, the size of one
-// 16384 x 8192 bf16 tensor.  Every access is a 16-byte vector load or store
-// with the nontemporal policy, as in the row kernels; each mix is timed over
-// grid-stride loops of several grid, block and unroll sizes and over a
-// row-chunked walk like the row kernels', and the best is kept.  "hot":
-// launches back to back; "cold": each launch after a 1 GiB write to other
-// memory.
+// one read per write (the forwards: x in, y out), two reads per write (the
+// backwards: x and dy in, dx out) and two reads per write in place (dx over
+// dy, as in the headline backward).  256 MiB per operand, the size of one
+// 16384 x 8192 bf16 tensor.  Every access is a 16-byte vector load or store.
+// The search covers, for every mix:
+//   * grid-stride loops: 32, 64 or 128 bytes of each input in flight per lane
+//     (2, 4 or 8 vectors), 256-, 512- and 1024-thread workgroups, grids of
+//     256 to 4096 workgroups;
+//   * row walks as the row kernels walk their tensors: rows of 16 KiB, 256-,
+//     512- or 1024-thread workgroups holding a row in 4, 2 or 1 vectors per
+//     lane (all of a row's loads before its stores), workgroup b taking rows
+//     b, b + grid, ...; persistent grids of 256 to 2048 workgroups and one
+//     row per workgroup (16384);
+// each with the nontemporal policy (as in the row kernels) and the default
+// one, and keeps the best.  "hot": launches back to back; "cold": each launch
+// after a 1 GiB write to other memory and a read of it (so no dirty line of
+// the write is left to be written back inside the timed launch).
 //
 // Prints one JSON line.  Run by bench.py (before it touches the GPU itself)
 // and usable on its own: tests/native/bin/stream_ceiling
@@ -17,6 +26,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #define CHECK(x)                                                                            \
@@ -30,13 +40,31 @@
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+template <bool NT>
+__device__ __forceinline__ u32x4 load(const u32x4* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store(u32x4* p, u32x4 v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+
 // Grid-stride over n 16-byte vectors, UNROLL loads of each input in flight
 // per thread.  Every index is below n (the loop condition covers the last
-// unrolled access); n is a multiple of UNROLL * stride for the shapes used,
-// so every vector is visited.
-template <int UNROLL, int READS, bool WRITE>
-__global__ void stream_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b, u32x4* __restrict__ c,
-                              u32x4* __restrict__ sink, long n) {
+// unrolled access); n is a multiple of UNROLL * stride for the shapes used
+// (powers of two, UNROLL * stride <= n), so every vector is visited.  c may
+// equal b.
+template <int UNROLL, int READS, bool WRITE, bool NT>
+__global__ void stream_kernel(const u32x4* a, const u32x4* b, u32x4* c, u32x4* __restrict__ sink, long n) {
   const long stride = static_cast<long>(gridDim.x) * blockDim.x;
   const long first = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -44,14 +72,14 @@ __global__ void stream_kernel(const u32x4* __restrict__ a, const u32x4* __restri
     u32x4 v[UNROLL], w[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      v[u] = __builtin_nontemporal_load(a + i + u * stride);
-      if (READS == 2) w[u] = __builtin_nontemporal_load(b + i + u * stride);
+      v[u] = load<NT>(a + i + u * stride);
+      if (READS == 2) w[u] = load<NT>(b + i + u * stride);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const u32x4 r = READS == 2 ? (v[u] ^ w[u]) : v[u];
       if (WRITE) {
-        __builtin_nontemporal_store(r, c + i + u * stride);
+        store<NT>(c + i + u * stride, r);
       } else {
         acc ^= r;
       }
@@ -60,27 +88,30 @@ __global__ void stream_kernel(const u32x4* __restrict__ a, const u32x4* __restri
   if (!WRITE) sink[first] = acc;  // keeps the loads; one vector per thread
 }
 
-// Row-chunked, as the row kernels walk their tensors: rows of 1024 vectors
-// (16 KiB), 512 threads x 2 vectors per row, workgroup b taking rows b,
-// b + grid, ...  Every index is below rows * 1024.
-template <int READS, bool WRITE>
-__global__ void rows_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b, u32x4* __restrict__ c,
-                            u32x4* __restrict__ sink, long rows) {
-  constexpr int kRowVecs = 1024;
+// Row walk: rows of kRowVecs vectors (16 KiB), a T-thread workgroup covering
+// a row with kRowVecs / T vectors per lane, all of them loaded before any is
+// stored; workgroup b takes rows b, b + grid, ...  Every index is below
+// rows * kRowVecs.  c may equal b (each lane reads its own vectors of b
+// before it writes them).
+constexpr int kRowVecs = 1024;
+template <int T, int READS, bool WRITE, bool NT>
+__global__ __launch_bounds__(T) void rows_kernel(const u32x4* a, const u32x4* b, u32x4* c, u32x4* __restrict__ sink,
+                                                 long rows) {
+  constexpr int kPer = kRowVecs / T;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (long r = blockIdx.x; r < rows; r += gridDim.x) {
     const long base = r * kRowVecs + threadIdx.x;
-    u32x4 v[2], w[2];
+    u32x4 v[kPer], w[kPer];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      v[u] = __builtin_nontemporal_load(a + base + u * 512);
-      if (READS == 2) w[u] = __builtin_nontemporal_load(b + base + u * 512);
+    for (int u = 0; u < kPer; ++u) {
+      v[u] = load<NT>(a + base + u * T);
+      if (READS == 2) w[u] = load<NT>(b + base + u * T);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kPer; ++u) {
       const u32x4 x = READS == 2 ? (v[u] ^ w[u]) : v[u];
       if (WRITE) {
-        __builtin_nontemporal_store(x, c + base + u * 512);
+        store<NT>(c + base + u * T, x);
       } else {
         acc ^= x;
       }
@@ -91,24 +122,27 @@ __global__ void rows_kernel(const u32x4* __restrict__ a, const u32x4* __restrict
 
 struct Result {
   double hot = 0, cold = 0;
-  char shape[48] = "";
+  char shape[64] = "";
   std::string all;  // "shape": hot GB/s, for every shape timed
 };
+
+// The four mixes: input count, whether the output is the second input.
+enum Mix { kRead, kCopy, kR2W1, kR2W1InPlace, kMixes };
 
 int main() {
   const long bytes = 256L << 20;
   const long n = bytes / 16;
+  const long rows = n / kRowVecs;
   const long flush_bytes = 1L << 30;
-  const int grids[] = {256, 512, 1024};
-  const int blocks[] = {256, 512};
-  const int row_grids[] = {512, 2048, 16384};
-  const long rows = n / 1024;
-  u32x4 *a, *b, *c, *sink;
-  void* flush;
+  const int grids[] = {256, 512, 1024, 2048, 4096};
+  const int row_grids[] = {256, 512, 1024, 2048, 16384};
+  u32x4 *a, *b, *c, *sink, *flush;
   CHECK(hipMalloc(&a, bytes));
   CHECK(hipMalloc(&b, bytes));
   CHECK(hipMalloc(&c, bytes));
-  CHECK(hipMalloc(&sink, 16384L * 512 * 16));  // one vector per thread of the largest grid
+  // one vector per thread of the largest grid of either kind
+  const long sink_vecs = std::max(4096L * 1024, 16384L * 1024);
+  CHECK(hipMalloc(&sink, sink_vecs * 16));
   CHECK(hipMalloc(&flush, flush_bytes));
   CHECK(hipMemset(a, 1, bytes));
   CHECK(hipMemset(b, 2, bytes));
@@ -116,6 +150,7 @@ int main() {
   hipEvent_t t0, t1;
   CHECK(hipEventCreate(&t0));
   CHECK(hipEventCreate(&t1));
+  const long flush_n = flush_bytes / 16;
 
   // bytes moved per launch: (reads + writes) operands of `bytes`
   auto measure = [&](auto launch, double operands, Result& best, const char* shape) {
@@ -130,8 +165,10 @@ int main() {
     CHECK(hipEventElapsedTime(&ms, t0, t1));
     const double hot = operands * bytes / (ms / reps * 1e-3) / 1e9;
     std::vector<float> cold_ms;
-    for (int k = 0; k < 7; ++k) {
+    for (int k = 0; k < 5; ++k) {
       CHECK(hipMemsetAsync(flush, k, flush_bytes));
+      // 4096 x 256 threads x 4 vectors: flush_n is a multiple of that stride
+      stream_kernel<4, 1, false, false><<<4096, 256>>>(flush, flush, flush, sink, flush_n);
       CHECK(hipEventRecord(t0));
       launch();
       CHECK(hipEventRecord(t1));
@@ -145,40 +182,68 @@ int main() {
       best.hot = hot;
       std::snprintf(best.shape, sizeof best.shape, "%s", shape);
     }
-    char item[96];
+    char item[112];
     std::snprintf(item, sizeof item, "%s\"%s\": %.0f", best.all.empty() ? "" : ", ", shape, hot);
     best.all += item;
     best.cold = std::max(best.cold, cold);
   };
 
-  Result read, copy, r2w1;
-  char shape[48];
+  Result res[kMixes];
+  char shape[64];
+  // one grid-stride shape for every mix, at one policy
+  auto stride_shapes = [&](auto unroll_tag, auto nt_tag, int g, int bs) {
+    constexpr int U = decltype(unroll_tag)::value;
+    constexpr bool NT = decltype(nt_tag)::value;
+    if (static_cast<long>(U) * g * bs > n) return;
+    const char* pol = NT ? "nt" : "default";
+    std::snprintf(shape, sizeof shape, "grid-stride %d B/lane, %d x %d, %s", U * 16, g, bs, pol);
+    measure([&] { stream_kernel<U, 1, false, NT><<<g, bs>>>(a, b, c, sink, n); }, 1.0, res[kRead], shape);
+    measure([&] { stream_kernel<U, 1, true, NT><<<g, bs>>>(a, b, c, sink, n); }, 2.0, res[kCopy], shape);
+    measure([&] { stream_kernel<U, 2, true, NT><<<g, bs>>>(a, b, c, sink, n); }, 3.0, res[kR2W1], shape);
+    measure([&] { stream_kernel<U, 2, true, NT><<<g, bs>>>(a, b, b, sink, n); }, 3.0, res[kR2W1InPlace], shape);
+  };
+  auto row_shapes = [&](auto t_tag, auto nt_tag, int g) {
+    constexpr int T = decltype(t_tag)::value;
+    constexpr bool NT = decltype(nt_tag)::value;
+    const char* pol = NT ? "nt" : "default";
+    std::snprintf(shape, sizeof shape, "16 KiB rows, %d x %d (%d vectors per lane), %s", g, T, kRowVecs / T, pol);
+    measure([&] { rows_kernel<T, 1, false, NT><<<g, T>>>(a, b, c, sink, rows); }, 1.0, res[kRead], shape);
+    measure([&] { rows_kernel<T, 1, true, NT><<<g, T>>>(a, b, c, sink, rows); }, 2.0, res[kCopy], shape);
+    measure([&] { rows_kernel<T, 2, true, NT><<<g, T>>>(a, b, c, sink, rows); }, 3.0, res[kR2W1], shape);
+    measure([&] { rows_kernel<T, 2, true, NT><<<g, T>>>(a, b, b, sink, rows); }, 3.0, res[kR2W1InPlace], shape);
+  };
+  using nt = std::true_type;
+  using dflt = std::false_type;
   for (int g : grids)
-    for (int bs : blocks) {
-      std::snprintf(shape, sizeof shape, "grid-stride x4, %d x %d", g, bs);
-      measure([&] { stream_kernel<4, 1, false><<<g, bs>>>(a, b, c, sink, n); }, 1.0, read, shape);
-      measure([&] { stream_kernel<4, 1, true><<<g, bs>>>(a, b, c, sink, n); }, 2.0, copy, shape);
-      measure([&] { stream_kernel<4, 2, true><<<g, bs>>>(a, b, c, sink, n); }, 3.0, r2w1, shape);
-      std::snprintf(shape, sizeof shape, "grid-stride x2, %d x %d", g, bs);
-      measure([&] { stream_kernel<2, 1, true><<<g, bs>>>(a, b, c, sink, n); }, 2.0, copy, shape);
-      measure([&] { stream_kernel<2, 2, true><<<g, bs>>>(a, b, c, sink, n); }, 3.0, r2w1, shape);
+    for (int bs : {256, 512, 1024}) {
+      stride_shapes(std::integral_constant<int, 2>{}, nt{}, g, bs);
+      stride_shapes(std::integral_constant<int, 4>{}, nt{}, g, bs);
+      stride_shapes(std::integral_constant<int, 8>{}, nt{}, g, bs);
+      stride_shapes(std::integral_constant<int, 2>{}, dflt{}, g, bs);
+      stride_shapes(std::integral_constant<int, 4>{}, dflt{}, g, bs);
+      stride_shapes(std::integral_constant<int, 8>{}, dflt{}, g, bs);
     }
   for (int g : row_grids) {
-    std::snprintf(shape, sizeof shape, "16 KiB rows, %d x 512", g);
-    measure([&] { rows_kernel<1, false><<<g, 512>>>(a, b, c, sink, rows); }, 1.0, read, shape);
-    measure([&] { rows_kernel<1, true><<<g, 512>>>(a, b, c, sink, rows); }, 2.0, copy, shape);
-    measure([&] { rows_kernel<2, true><<<g, 512>>>(a, b, c, sink, rows); }, 3.0, r2w1, shape);
+    row_shapes(std::integral_constant<int, 256>{}, nt{}, g);
+    row_shapes(std::integral_constant<int, 512>{}, nt{}, g);
+    row_shapes(std::integral_constant<int, 1024>{}, nt{}, g);
+    row_shapes(std::integral_constant<int, 256>{}, dflt{}, g);
+    row_shapes(std::integral_constant<int, 512>{}, dflt{}, g);
+    row_shapes(std::integral_constant<int, 1024>{}, dflt{}, g);
   }
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
   auto obj = [](const Result& r) {
-    char head[160];
+    char head[200];
     std::snprintf(head, sizeof head, "{\"hot_gbps\": %.0f, \"cold_gbps\": %.0f, \"best_hot_shape\": \"%s\", ", r.hot,
                   r.cold, r.shape);
     return std::string(head) + "\"hot_gbps_by_shape\": {" + r.all + "}}";
   };
-  std::printf("{\"bytes_per_operand\": %ld, \"read\": %s, \"read1_write1\": %s, \"read2_write1\": %s}\n", bytes,
-              obj(read).c_str(), obj(copy).c_str(), obj(r2w1).c_str());
+  std::printf(
+      "{\"bytes_per_operand\": %ld, \"read\": %s, \"read1_write1\": %s, \"read2_write1\": %s, "
+      "\"read2_write1_in_place\": %s}\n",
+      bytes, obj(res[kRead]).c_str(), obj(res[kCopy]).c_str(), obj(res[kR2W1]).c_str(),
+      obj(res[kR2W1InPlace]).c_str());
   CHECK(hipFree(a));
   CHECK(hipFree(b));
   CHECK(hipFree(c));
