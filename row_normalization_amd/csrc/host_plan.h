@@ -271,7 +271,38 @@ inline int64_t workgroups_per_cu(const RowPlan& p) {
 // rows of two vectors at N = 7168: 1-6 % slower), and with 2-4 row groups
 // per workgroup (4096 x 4096, LayerNorm at 4096 x 2048) the rows of a
 // workgroup queue behind each other (3-15 % slower).
-inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int es) {
+// A few row steps: 16-bit rows of at least kFwdFewStepsMinRowBytes and at
+// most kFwdFewStepsMaxWaves waves, where a grid of kFwdFewStepsGrid
+// workgroups of one row group each (four per CU, all resident at once) gives
+// every workgroup 3 to 6 row steps (LayerNorm; 3 to 4 for RMSNorm), run as
+// that persistent grid: every CU gets the same rows, where the dispatcher's
+// rounds of one-row-group workgroups leave the last round part empty, and
+// each workgroup loads the weights once.  Measured on MI355X (interleaved
+// comparison, fp16 LayerNorm): M = 3000 to 6144, N = 3584-7168 3-13 % faster
+// (the chapter's M = 4096 sweep: N = 3584 7 %, 4096 9 %, 4608 9 %, 5120
+// 10 %, 5632 13 %, 6144 12 %, 6656 10 %, 7168 9 %, 8704-10240 6-8 %);
+// 3072 (6 KiB rows) -4 ... +1 %; rows of 6-7 waves of four vectors, which
+// the rules above run persistent with two workgroups per CU, 3-14 % slower
+// (N = 10752-14336: four of their workgroups do not all fit a CU); at
+// M = 8192 -7 ... +4 % and M = 16384 -7 ... +8 %, M = 2048 -15 ... +19 %,
+// M = 1024 -4 ... +3 %, so those keep the rules above; RMSNorm bf16 M = 3000
+// and 4096, N = 3072-5120 1-8 % faster (the 4096 x 4096 workload 1 %),
+// M = 5000 and 6144 0-1 % slower.
+constexpr int64_t kFwdFewStepsGrid = 4 * kComputeUnits;
+constexpr int64_t kFwdFewStepsMin = 3;
+constexpr int64_t kFwdFewStepsMaxLn = 6;
+constexpr int64_t kFwdFewStepsMaxRms = 4;
+constexpr int64_t kFwdFewStepsMinRowBytes = 7168;
+constexpr int kFwdFewStepsMaxWaves = 5;
+inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int64_t N, int es) {
+  const int64_t few_steps = ceil_div(M, kFwdFewStepsGrid);
+  if (es == 2 && N * es >= kFwdFewStepsMinRowBytes && p.wpr <= kFwdFewStepsMaxWaves && few_steps >= kFwdFewStepsMin &&
+      few_steps <= (op == RowOp::kLnFwd ? kFwdFewStepsMaxLn : kFwdFewStepsMaxRms)) {
+    p.rpb = 1;
+    p.grid = kFwdFewStepsGrid;
+    p.row_iters = few_steps;
+    return;
+  }
   p.rpb = std::max(1, kBlockWaves / p.wpr);
   const int64_t groups = ceil_div(M, p.rpb);
   const int64_t per_cu = workgroups_per_cu(p);
@@ -357,7 +388,7 @@ inline RowPlan plan_rows(RowOp op, int64_t M, int64_t N, int vec, int dtype) {
   if (backward)
     plan_bwd_grid(p, op, M, es, dtype);
   else
-    plan_fwd_grid(p, op, M, es);
+    plan_fwd_grid(p, op, M, N, es);
   return p;
 }
 

@@ -67,14 +67,17 @@ def test_small_shapes(dtype, M, N):
 # backward rows of 5-8 waves run as one workgroup of two or three row groups
 # per CU with the next row's loads in flight; rows of 1-4 waves where the
 # partial rows are a large share run one workgroup of their own shape per CU,
-# pipelined, as well.  Each in place and not, with the split and the fused
-# backward.
+# pipelined, as well; and forwards of 3-6 row steps run as 1024 persistent
+# workgroups of one row group.  Each in place and not, with the split and the
+# fused backward.
 LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16", 4100, 6144), ("f32", 3000, 4096),
          ("f16", 4097, 8192), ("bf16", 4100, 8192), ("f16", 2049, 5120),
          # rows of 1-4 waves, one workgroup per CU, next row's loads in flight
          ("f16", 4100, 1024), ("f16", 4096, 2048), ("f16", 4096, 3072), ("f32", 4096, 2048), ("f16", 1000, 8192),
          # bf16 rows of 4-8 waves, not pipelined: one 16-wave workgroup per CU
-         ("bf16", 4096, 4096), ("bf16", 1151, 8192), ("bf16", 4097, 6144)]
+         ("bf16", 4096, 4096), ("bf16", 1151, 8192), ("bf16", 4097, 6144),
+         # forward of 3-6 row steps: 1024 persistent workgroups of one row group
+         ("f16", 6000, 5632), ("bf16", 5000, 3584), ("f16", 2100, 7168)]
 
 
 @pytest.mark.parametrize("dtype,M,N", LARGE, ids=[f"{d}-{m}x{n}" for d, m, n in LARGE])

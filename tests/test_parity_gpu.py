@@ -134,6 +134,10 @@ SMALL = [
     ("bf16", 3000, 3072, False, False), # 3 x 2, two row groups (6 waves)
     ("f32", 4097, 1024, False, True),   # fp32 4 x 1 x 2
     ("bf16", 1151, 8192, True, True),   # 8 x 2 rows, 16-wave workgroups, 144 of them, 4 steps
+    # forward of 3-4 row steps: 1024 persistent workgroups of one row group
+    ("bf16", 4096, 4096, False, True),  # 4 x 2, 4 steps
+    ("f16", 3500, 5120, True, False),   # 5 x 2, 4 steps, the last ragged
+    ("bf16", 2049, 3584, False, False), # 4 x 2, 3 steps, one row in the last
 ]
 
 
