@@ -8,7 +8,8 @@
 // matters.  For 16-bit LayerNorm rows beyond RMSNORM_N_MAX (up to
 // LAYERNORM_N_MAX_16BIT) it checks that the wide plan covers the row within
 // the wide kernels' registers, and that the backward over 16-byte vectors
-// gets a chunk count its held-row kernel is compiled for.  Built and
+// gets a chunk count its held-row kernel is compiled for.  It pins the
+// grids the grid rules pick at a few shapes as well.  Built and
 // run by tests/test_plan.py; prints one summary line and exits non-zero on
 // failure.
 #include <cstdio>
@@ -173,6 +174,54 @@ int main(int argc, char** argv) {
       ++bad;
       std::printf("shape pin: es=%d N=%ld op=%d: got %d x %d, expected %d x %d\n", q.es, static_cast<long>(q.N),
                   static_cast<int>(q.op), p.wpr, p.iters, q.wpr, q.iters);
+    }
+  }
+  // grids the planner's rules pick, 16-byte vectors: (element size, M, N,
+  // op, dtype, workgroups, row groups per workgroup, row steps, pipelined
+  // backward: 1 / 0, -1 for a forward)
+  struct GridPin {
+    int es;
+    int64_t M, N;
+    RowOp op;
+    int dtype;
+    int64_t grid;
+    int rpb;
+    int64_t row_iters;
+    int pipelined;
+  };
+  const GridPin grid_pins[] = {
+      // backward: one pipelined workgroup of the row's shape per CU wherever
+      // the pipelined loop is compiled
+      {2, 16384, 8192, RowOp::kRmsBwd, 1, 256, 1, 64, 1},    // the headline
+      {2, 32768, 5120, RowOp::kRmsBwd, 1, 256, 1, 128, 1},   // 5-wave rows alone on a CU
+      {2, 4096, 4096, RowOp::kRmsBwd, 1, 256, 2, 8, 1},      // 4-wave rows, two row groups
+      {2, 32768, 4096, RowOp::kLnBwd, 2, 256, 2, 64, 1},
+      // ... 16-wave workgroups for 5-8-wave rows where the partial rows weigh
+      {2, 4096, 6144, RowOp::kLnBwd, 2, 256, 2, 8, 1},
+      // ... and two per CU where the loop is not compiled (bf16 LayerNorm)
+      {2, 32768, 4096, RowOp::kLnBwd, 1, 512, 2, 32, 0},
+      // forward of 3-6 row steps (LayerNorm; 3-4 RMSNorm): 1024 workgroups of
+      // one row group, for rows of >= 7 KiB and <= 5 waves
+      {2, 4096, 4096, RowOp::kLnFwd, 2, 1024, 1, 4, -1},
+      {2, 4096, 4096, RowOp::kRmsFwd, 1, 1024, 1, 4, -1},
+      {2, 6000, 5632, RowOp::kLnFwd, 2, 1024, 1, 6, -1},
+      {2, 2049, 3584, RowOp::kRmsFwd, 1, 1024, 1, 3, -1},
+      {2, 6000, 4096, RowOp::kRmsFwd, 1, 3000, 2, 1, -1},    // 6 steps: RMSNorm keeps the other rules
+      {2, 4096, 3072, RowOp::kLnFwd, 2, 2048, 2, 1, -1},     // 6 KiB rows
+      {2, 4096, 12288, RowOp::kLnFwd, 2, 512, 1, 8, -1},     // 6-wave rows of four vectors: persistent, two per CU
+      {2, 2048, 6144, RowOp::kLnFwd, 2, 1024, 2, 1, -1},     // 2 steps: one workgroup per two 3 x 4 row groups
+  };
+  for (const GridPin& q : grid_pins) {
+    const RowPlan p = plan_rows(q.op, q.M, q.N, 16 / q.es, q.dtype);
+    ++n;
+    const int pipe = q.op == RowOp::kRmsBwd || q.op == RowOp::kLnBwd ? int(bwd_pipelined(q.op, p, q.dtype)) : -1;
+    if (p.grid != q.grid || p.rpb != q.rpb || p.row_iters != q.row_iters || pipe != q.pipelined) {
+      ++bad;
+      std::printf("grid pin: op=%d dtype=%d %ld x %ld: got grid %ld, %d row groups, %ld steps, pipelined %d; expected "
+                  "%ld, %d, %ld, %d\n",
+                  static_cast<int>(q.op), q.dtype, static_cast<long>(q.M), static_cast<long>(q.N),
+                  static_cast<long>(p.grid), p.rpb, static_cast<long>(p.row_iters), pipe, static_cast<long>(q.grid),
+                  q.rpb, static_cast<long>(q.row_iters), q.pipelined);
     }
   }
   std::printf("checked %ld plans, %ld bad\n", n, bad);
