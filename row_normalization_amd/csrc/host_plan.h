@@ -176,12 +176,21 @@ inline bool row_shape(int64_t nvec, int iters_cap, int target, bool narrow, bool
 // their shape; one workgroup per CU of fewer than kBwdMinGridWaves / 256
 // waves was slower (4096 x 1024 with 128 workgroups of 8 waves: 13 %).
 constexpr double kBwdWideShare = 0.03;
-// Where the pipelined loop is not compiled for the plan (bf16 LayerNorm, whose
-// unpacking needs more registers; narrower vectors), only rows of 4-8 waves
-// run one 16-wave workgroup per CU (two to four row groups keep each other's
-// loads in flight), and only above kBwdWideShareUnpipelined.  Measured on
-// MI355X, LayerNorm bf16 full backward: 4096 x 4096 (share 0.33) 9 %, 4096 x
-// 8192 (0.17) 3 %, 4096 x 6144 (0.17) 1.8 %, 1151 x 8192 (0.59) 21 % faster;
+// The bf16 LayerNorm backward pipelines only in its build for workgroups of
+// at most kNarrowThreads threads (launch.h): there, rows of 1-4 waves (in
+// workgroups of 6-8 waves) and rows of 8 waves where the partial rows are
+// light run one workgroup per CU, pipelined.  Measured on MI355X
+// (interleaved comparison, full backward) against the plans below: 4096 x
+// 1024-4096 9-15 % faster, 8192 x 2048 8 %, 16384 x 2048 and 4096 4.5 and
+// 3 %, 32768 x 4096 1.5 %, 16384 x 8192 5 %; rows of 5-7 waves alone on a
+// CU were slower (16384 x 5120 17 %, 16384 and 32768 x 6144 4-5 %) and keep
+// the plans below.
+// Where the pipelined loop is not compiled for the plan (narrower vectors;
+// the bf16 LayerNorm rows above), only rows of 4-8 waves run one 16-wave
+// workgroup per CU (two to four row groups keep each other's loads in
+// flight), and only above kBwdWideShareUnpipelined.  Measured on MI355X,
+// LayerNorm bf16 full backward: 4096 x 4096 (share 0.33) 9 %, 4096 x 8192
+// (0.17) 3 %, 4096 x 6144 (0.17) 1.8 %, 1151 x 8192 (0.59) 21 % faster;
 // 16384 x 6432 (0.042) 5 % slower; rows of 1-3 waves (4096 x 1024-3072, 16
 // row groups to combine) 0.5-22 % slower, as was fp32 RMSNorm 4096 x 1001.
 constexpr double kBwdWideShareUnpipelined = 0.1;
@@ -325,9 +334,12 @@ inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int64_t N, int es) {
 //      per CU; where the partial rows of the grid of step 1 exceed
 //      kBwdWideShare of the row traffic, rows of 5-8 waves two to a 16-wave
 //      workgroup (bwd_partials_heavy);
-//   3. where the pipelined loop is not compiled: rows of 4-8 waves as one
+//   3. where only the narrow build pipelines (bf16 LayerNorm): one workgroup
+//      per CU for rows of 1-4 waves, and of 8 waves below
+//      kBwdWideShareUnpipelined;
+//   4. where the pipelined loop is not compiled: rows of 4-8 waves as one
 //      16-wave workgroup per CU, above kBwdWideShareUnpipelined only;
-//   4. with one workgroup per CU: at least kBwdMinSteps row steps each while
+//   5. with one workgroup per CU: at least kBwdMinSteps row steps each while
 //      the grid keeps kBwdMinGridWaves waves, then the fewest workgroups that
 //      keep the step count and those waves.
 // Pipelining (bwd_pipelined) and the partial rows' store policy
@@ -338,13 +350,17 @@ inline void plan_bwd_grid(RowPlan& p, RowOp op, int64_t M, int es, int dtype) {
   int64_t per_cu = workgroups_per_cu(p);
   const int64_t default_grid = std::min(groups, std::min(kBwdGridMax, kComputeUnits * per_cu));
   const bool fits = bwd_pipeline_fits(op, dtype, p.vec, p.iters);
+  const bool fits_narrow = bwd_pipeline_fits(op, dtype, p.vec, p.iters, kNarrowThreads) && p.threads() <= kNarrowThreads;
   const bool rows_4_to_8 = p.wpr * 2 >= kBlockWaves && p.wpr <= kBlockWaves;
   const bool rows_5_to_8 = p.wpr * 2 > kBlockWaves && p.wpr <= kBlockWaves;
+  const bool heavy_unpipelined = bwd_partials_heavy(op, M, es, default_grid, kBwdWideShareUnpipelined);
   bool sixteen_waves = false;
   if (fits) {
     sixteen_waves = rows_5_to_8 && bwd_partials_heavy(op, M, es, default_grid);
     per_cu = 1;
-  } else if (!fits && rows_4_to_8 && bwd_partials_heavy(op, M, es, default_grid, kBwdWideShareUnpipelined)) {
+  } else if (fits_narrow && (p.wpr <= kBlockWaves / 2 || (p.wpr == kBlockWaves && !heavy_unpipelined))) {
+    per_cu = 1;  // the bf16 LayerNorm backward, pipelined in its narrow build
+  } else if (rows_4_to_8 && heavy_unpipelined) {
     sixteen_waves = true;
     per_cu = 1;
   }
@@ -444,7 +460,7 @@ inline RowPlan plan_ln_fwd(int64_t M, int64_t N, int vec, int dtype) {
 // gives two workgroups per CU only where the pipelined loop is not compiled.)
 inline bool bwd_pipelined(RowOp op, const RowPlan& p, int dtype) {
   const bool alone_on_cu = p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits;
-  return alone_on_cu && bwd_pipeline_fits(op, dtype, p.vec, p.iters);
+  return alone_on_cu && bwd_pipeline_fits(op, dtype, p.vec, p.iters, p.threads());
 }
 
 // Whether the backward writes its partial rows (tables x grid x N fp32)

@@ -210,12 +210,22 @@ constexpr int lane_elems_cap(RowOp op, int elsize) {
 // registers.  It is compiled, and chosen, only where a lane holds at most
 // two full 16-byte vectors of each operand (beyond that, or with narrower
 // vectors and so more loads and offsets per row, the second row would
-// spill), and not for the bf16 LayerNorm backward: its third per-column
-// table (the db partials) and bf16's unpacking take ~140 registers with two
-// rows in flight, past the 128 a lane of a 16-wave workgroup has.
+// spill), and for the bf16 LayerNorm backward only in its build for
+// workgroups of at most kNarrowThreads threads: its third per-column table
+// (the db partials) and bf16's unpacking take ~140 registers with two rows
+// in flight, past the 128 a lane of a 1024-thread workgroup has, within the
+// 256 of a 512-thread one (two waves per SIMD).  `max_threads` is the
+// workgroup size the build is bounded to.
 constexpr int kPipelineLaneVectors = 2;
-constexpr bool bwd_pipeline_fits(RowOp op, int dtype, int vec, int iters) {
-  return vec * (dtype == 0 ? 4 : 2) == 16 && iters <= kPipelineLaneVectors && !(op == RowOp::kLnBwd && dtype == 1);
+constexpr int kNarrowThreads = 512;
+constexpr bool bwd_pipeline_fits(RowOp op, int dtype, int vec, int iters, int max_threads = 1024) {
+  return vec * (dtype == 0 ? 4 : 2) == 16 && iters <= kPipelineLaneVectors &&
+         !(op == RowOp::kLnBwd && dtype == 1 && max_threads > kNarrowThreads);
+}
+// Whether a pipelined plan needs the build bounded to kNarrowThreads-thread
+// workgroups (the bf16 LayerNorm backward).
+constexpr bool bwd_needs_narrow_build(RowOp op, int dtype, int vec, int iters) {
+  return !bwd_pipeline_fits(op, dtype, vec, iters) && bwd_pipeline_fits(op, dtype, vec, iters, kNarrowThreads);
 }
 
 // Tile of the dgamma reduction: kReduceCols column threads (a 128-byte row

@@ -234,8 +234,8 @@ __device__ __forceinline__ void ln_bwd_process_row(LnBwdRow<S, VEC, ITERS>& t, c
   }
 }
 
-template <typename S, int VEC, int ITERS>
-__global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArgs a) {
+template <typename S, int VEC, int ITERS, int MAXT>
+__global__ __launch_bounds__(MAXT) void layernorm_bwd_rows_kernel(const LnBwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float comb[];  // 2N floats, when rpb > 1
   __shared__ float red[2][2][kMaxBlockWaves];
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(1024) void layernorm_bwd_rows_kernel(const LnBwdArg
   }
 
   bool pipelined = false;
-  if constexpr (bwd_pipeline_fits(RowOp::kLnBwd, dtype_code<S>(), VEC, ITERS)) pipelined = a.pipeline;
+  if constexpr (bwd_pipeline_fits(RowOp::kLnBwd, dtype_code<S>(), VEC, ITERS, MAXT)) pipelined = a.pipeline;
   if (pipelined) {
     // One workgroup per CU: the next row's loads are in flight during this
     // row's sums, barrier and stores.  Unconditional loads over an even
@@ -755,7 +755,17 @@ hipError_t ln_bwd_inst(const RowPlan& p, const LnBwdArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;  // beyond the register model: never planned, not compiled
   } else {
     const size_t lds = p.rpb > 1 ? 2 * static_cast<size_t>(a.N) * sizeof(float) : 0;
-    hipLaunchKernelGGL((layernorm_bwd_rows_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)),
+    if constexpr (bwd_needs_narrow_build(RowOp::kLnBwd, dtype_code<S>(), VEC, ITERS)) {
+      // pipelined only in the build for workgroups of at most kNarrowThreads
+      // threads, which the planner keeps to
+      if (a.pipeline) {
+        if (p.threads() > kNarrowThreads) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((layernorm_bwd_rows_kernel<S, VEC, ITERS, kNarrowThreads>), dim3(static_cast<unsigned>(p.grid)),
+                           dim3(p.threads()), lds, s, a);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((layernorm_bwd_rows_kernel<S, VEC, ITERS, 1024>), dim3(static_cast<unsigned>(p.grid)),
                        dim3(p.threads()), lds, s, a);
     return hipGetLastError();
   }

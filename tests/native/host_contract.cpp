@@ -80,7 +80,7 @@ hipError_t launch_bwd_rows(int dtype, const RowPlan& p, const BwdArgs& a, hipStr
   ++g_launches;
   check_row_plan(p, RowOp::kRmsBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 4 <= 65536, "LDS combine size", a.N);
-  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kRmsBwd, dtype, p.vec, p.iters) &&
+  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kRmsBwd, dtype, p.vec, p.iters, p.threads()) &&
                          (p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits)),
          "pipelined only where it fits and the workgroup is alone on its CU");
   expect(p.grid <= partial_rows_bound(a.M), "partial rows within the workspace", p.grid);
@@ -109,7 +109,7 @@ hipError_t launch_ln_bwd_rows(int dtype, const RowPlan& p, const LnBwdArgs& a, h
   check_row_plan(p, RowOp::kLnBwd, dtype, a.M, a.stride, a.N, a.nvec, a.wpr, a.rpb, a.row_iters);
   expect(p.rpb == 1 || int64_t(a.N) * 8 <= 65536, "LDS combine size", a.N);
   expect(a.partials_nt == int(partials_nontemporal(2, p.grid, a.N)), "partial-row store policy", p.grid, a.N);
-  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kLnBwd, dtype, p.vec, p.iters) &&
+  expect(!a.pipeline || (bwd_pipeline_fits(RowOp::kLnBwd, dtype, p.vec, p.iters, p.threads()) &&
                          (p.wpr * p.rpb * 2 > kBwdResidentWaves || p.grid <= kComputeUnits)),
          "pipelined only where it fits and the workgroup is alone on its CU");
   return hipSuccess;

@@ -198,8 +198,12 @@ int main(int argc, char** argv) {
       {2, 32768, 4096, RowOp::kLnBwd, 2, 256, 2, 64, 1},
       // ... 16-wave workgroups for 5-8-wave rows where the partial rows weigh
       {2, 4096, 6144, RowOp::kLnBwd, 2, 256, 2, 8, 1},
-      // ... and two per CU where the loop is not compiled (bf16 LayerNorm)
-      {2, 32768, 4096, RowOp::kLnBwd, 1, 512, 2, 32, 0},
+      // bf16 LayerNorm: pipelined in its build for workgroups of at most 512
+      // threads, except rows of 5-8 waves where the partial rows weigh (one
+      // 16-wave workgroup per CU, not pipelined)
+      {2, 32768, 4096, RowOp::kLnBwd, 1, 256, 2, 64, 1},
+      {2, 4096, 4096, RowOp::kLnBwd, 1, 256, 2, 8, 1},
+      {2, 4096, 6144, RowOp::kLnBwd, 1, 256, 2, 8, 0},
       // forward of 3-6 row steps (LayerNorm; 3-4 RMSNorm): 1024 workgroups of
       // one row group, for rows of >= 7 KiB and <= 5 waves
       {2, 4096, 4096, RowOp::kLnFwd, 2, 1024, 1, 4, -1},

@@ -77,7 +77,10 @@ LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16"
          # bf16 rows of 4-8 waves, not pipelined: one 16-wave workgroup per CU
          ("bf16", 4096, 4096), ("bf16", 1151, 8192), ("bf16", 4097, 6144),
          # forward of 3-6 row steps: 1024 persistent workgroups of one row group
-         ("f16", 6000, 5632), ("bf16", 5000, 3584), ("f16", 2100, 7168)]
+         ("f16", 6000, 5632), ("bf16", 5000, 3584), ("f16", 2100, 7168),
+         # bf16 backward pipelined in its build for workgroups of at most 512
+         # threads: rows of 1-4 waves, and of 8 waves where the partial rows are light
+         ("bf16", 4100, 1024), ("bf16", 3000, 3072), ("bf16", 9000, 8192)]
 
 
 @pytest.mark.parametrize("dtype,M,N", LARGE, ids=[f"{d}-{m}x{n}" for d, m, n in LARGE])
