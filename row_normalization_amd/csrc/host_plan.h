@@ -297,20 +297,54 @@ inline int64_t workgroups_per_cu(const RowPlan& p) {
 // M = 1024 -4 ... +3 %, so those keep the rules above; RMSNorm bf16 M = 3000
 // and 4096, N = 3072-5120 1-8 % faster (the 4096 x 4096 workload 1 %),
 // M = 5000 and 6144 0-1 % slower.
+// Shorter 16-bit rows (more than kFwdFewStepsShortMinRowBytes, less than
+// kFwdFewStepsMinRowBytes; 16-byte vectors): where the rows divide evenly into
+// 2 to 6 row steps (LayerNorm; 2 to 4 for RMSNorm) of workgroups of up to
+// kFwdFewStepsShortGroups row groups (kBlockWaves waves at most), on a
+// whole number of workgroups per CU (at most four), so that every CU and
+// every workgroup takes the same rows, the forward runs as that persistent
+// grid.  Measured on MI355X (interleaved comparison against the rules
+// below): LayerNorm fp16 N = 2576-3456 (rows of 3-4 waves, two per
+// workgroup) at M = 3072, 4096, 6144, 8192, 12288: -1 ... -13 % (the
+// chapter's M = 4096 sweep at N = 3072: 11 %), N = 1280-2560 (rows of 1-2
+// waves, four per workgroup) at M = 6144-16384: -4 ... -18 % (2048: -4 ...
+// +1 % at 3-4 steps); RMSNorm bf16 -1 ... -10 % in the same places.  Where
+// the rows do not divide evenly (M = 2100, 2500, 5000, 10000, 14000) the
+// same grids, balanced or of four workgroups per CU, ran up to 27 % slower:
+// a static grid then leaves some CUs more rows, where the dispatcher
+// balances one-step workgroups.  Rows of at most 2 KiB (one or two vectors
+// per lane in one wave) were -9 ... +11 %.
 constexpr int64_t kFwdFewStepsGrid = 4 * kComputeUnits;
 constexpr int64_t kFwdFewStepsMin = 3;
 constexpr int64_t kFwdFewStepsMaxLn = 6;
 constexpr int64_t kFwdFewStepsMaxRms = 4;
 constexpr int64_t kFwdFewStepsMinRowBytes = 7168;
 constexpr int kFwdFewStepsMaxWaves = 5;
+constexpr int kFwdFewStepsShortGroups = 4;
+constexpr int64_t kFwdFewStepsShortMinRowBytes = 2048;
+constexpr int64_t kFwdFewStepsShortMin = 2;
 inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int64_t N, int es) {
+  const int64_t max_steps = op == RowOp::kLnFwd ? kFwdFewStepsMaxLn : kFwdFewStepsMaxRms;
   const int64_t few_steps = ceil_div(M, kFwdFewStepsGrid);
   if (es == 2 && N * es >= kFwdFewStepsMinRowBytes && p.wpr <= kFwdFewStepsMaxWaves && few_steps >= kFwdFewStepsMin &&
-      few_steps <= (op == RowOp::kLnFwd ? kFwdFewStepsMaxLn : kFwdFewStepsMaxRms)) {
+      few_steps <= max_steps) {
     p.rpb = 1;
     p.grid = kFwdFewStepsGrid;
     p.row_iters = few_steps;
     return;
+  }
+  if (es == 2 && p.vec * es == 16 && N * es > kFwdFewStepsShortMinRowBytes && N * es < kFwdFewStepsMinRowBytes) {
+    // rows per CU and row step with one workgroup per CU
+    const int rpb = std::max(1, std::min(kFwdFewStepsShortGroups, kBlockWaves / p.wpr));
+    const int64_t cu_step_rows = int64_t(rpb) * kComputeUnits;
+    const int64_t units = M / cu_step_rows;
+    const int64_t steps = ceil_div(units, kFwdFewStepsGrid / kComputeUnits);
+    if (M % cu_step_rows == 0 && steps >= kFwdFewStepsShortMin && steps <= max_steps && units % steps == 0) {
+      p.rpb = rpb;
+      p.row_iters = steps;
+      p.grid = units / steps * kComputeUnits;
+      return;
+    }
   }
   p.rpb = std::max(1, kBlockWaves / p.wpr);
   const int64_t groups = ceil_div(M, p.rpb);

@@ -211,7 +211,16 @@ int main(int argc, char** argv) {
       {2, 6000, 5632, RowOp::kLnFwd, 2, 1024, 1, 6, -1},
       {2, 2049, 3584, RowOp::kRmsFwd, 1, 1024, 1, 3, -1},
       {2, 6000, 4096, RowOp::kRmsFwd, 1, 3000, 2, 1, -1},    // 6 steps: RMSNorm keeps the other rules
-      {2, 4096, 3072, RowOp::kLnFwd, 2, 2048, 2, 1, -1},     // 6 KiB rows
+      // ... and rows of 2-7 KiB where the rows divide evenly into 2-6 steps
+      // (2-4 RMSNorm) over a whole number of workgroups per CU, at most four
+      {2, 4096, 3072, RowOp::kLnFwd, 2, 1024, 2, 2, -1},     // 3-wave rows, two per workgroup
+      {2, 4096, 3328, RowOp::kRmsFwd, 1, 1024, 2, 2, -1},    // 4-wave rows
+      {2, 12288, 2816, RowOp::kLnFwd, 2, 1024, 2, 6, -1},
+      {2, 12288, 2816, RowOp::kRmsFwd, 1, 6144, 2, 1, -1},   // 6 steps: RMSNorm keeps the other rules
+      {2, 6144, 2304, RowOp::kLnFwd, 2, 768, 4, 2, -1},      // 1-wave rows, four per workgroup
+      {2, 16384, 2048, RowOp::kRmsFwd, 1, 1024, 4, 4, -1},   // 2-wave rows
+      {2, 5000, 3072, RowOp::kLnFwd, 2, 2500, 2, 1, -1},     // rows that do not divide evenly
+      {2, 8192, 1024, RowOp::kLnFwd, 2, 1024, 8, 1, -1},     // 2 KiB rows
       {2, 4096, 12288, RowOp::kLnFwd, 2, 512, 1, 8, -1},     // 6-wave rows of four vectors: persistent, two per CU
       {2, 2048, 6144, RowOp::kLnFwd, 2, 1024, 2, 1, -1},     // 2 steps: one workgroup per two 3 x 4 row groups
   };

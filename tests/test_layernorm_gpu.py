@@ -67,9 +67,10 @@ def test_small_shapes(dtype, M, N):
 # backward rows of 5-8 waves run as one workgroup of two or three row groups
 # per CU with the next row's loads in flight; rows of 1-4 waves where the
 # partial rows are a large share run one workgroup of their own shape per CU,
-# pipelined, as well; and forwards of 3-6 row steps run as 1024 persistent
-# workgroups of one row group.  Each in place and not, with the split and the
-# fused backward.
+# pipelined, as well; forwards of 3-6 row steps run as 1024 persistent
+# workgroups of one row group, and forwards of shorter rows as persistent
+# grids of two to four row groups per workgroup where the rows divide
+# evenly.  Each in place and not, with the split and the fused backward.
 LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16", 4100, 6144), ("f32", 3000, 4096),
          ("f16", 4097, 8192), ("bf16", 4100, 8192), ("f16", 2049, 5120),
          # rows of 1-4 waves, one workgroup per CU, next row's loads in flight
@@ -78,6 +79,10 @@ LARGE = [("f16", 8200, 5264), ("bf16", 16384, 6432), ("f16", 8195, 9216), ("f16"
          ("bf16", 4096, 4096), ("bf16", 1151, 8192), ("bf16", 4097, 6144),
          # forward of 3-6 row steps: 1024 persistent workgroups of one row group
          ("f16", 6000, 5632), ("bf16", 5000, 3584), ("f16", 2100, 7168),
+         # rows of 2-7 KiB dividing evenly into row steps of a persistent grid
+         # (4096 x 3072 above: 1024 workgroups of two 3-wave rows, two steps;
+         # 768 workgroups of four 1-wave rows, and of two 4-wave rows, two steps)
+         ("bf16", 6144, 2304), ("f16", 3072, 3328),
          # bf16 backward pipelined in its build for workgroups of at most 512
          # threads: rows of 1-4 waves, and of 8 waves where the partial rows are light
          ("bf16", 4100, 1024), ("bf16", 3000, 3072), ("bf16", 9000, 8192)]

@@ -115,6 +115,10 @@ SMALL = [
     ("f32", 150, 704, False, False),    # 2 x 2
     ("f32", 90, 1600, True, True),      # 4 x 2
     ("bf16", 129, 1096, False, False),  # forward one wave of 4
+    # forward rows of 2-7 KiB dividing evenly into two row steps of a
+    # persistent grid of 768 workgroups (four 2-wave rows, two 3-wave rows)
+    ("bf16", 6144, 1792, True, True),
+    ("f16", 3072, 2816, False, False),
     # backward rows of 5-8 waves where the partial rows would be a large share
     # of the traffic: one workgroup of two or three row groups per CU, the
     # next row's loads in flight (odd numbers of row steps: the loop runs one
