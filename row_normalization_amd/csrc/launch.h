@@ -46,6 +46,8 @@ struct FwdArgs {
   int32_t rpb;
   int64_t row_iters;
   int32_t round_normed;  // 1: round x*r to the I/O type before the weight multiply
+  int32_t first_row_early;  // host side: launch the build that issues the first row's loads before
+                            // unpacking the weight (fwd_first_row_early)
 };
 
 struct BwdArgs {

@@ -136,6 +136,7 @@ int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t 
   a.rpb = p.rpb;
   a.row_iters = p.row_iters;
   a.round_normed = (flags & RMSNORM_ROUND_NORMED) && dtype != RMSNORM_F32;
+  a.first_row_early = fwd_first_row_early(p);
   return hip_status(launch_fwd(dtype, p, a, stream));
 }
 

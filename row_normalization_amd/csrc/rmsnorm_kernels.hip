@@ -74,7 +74,51 @@ constexpr int kBwdStoreDx = kNontemporal;
 // through the rows).  gamma is loaded once per workgroup and kept packed in
 // registers across its rows.
 // ---------------------------------------------------------------------------
+// One forward row's work once its x is in registers: r (written by one lane
+// of the row group), then y.
 template <typename S, int VEC, int ITERS>
+__device__ __forceinline__ void fwd_row(Pack<S, VEC> (&xv)[ITERS], const Pack<S, VEC> (&gv)[ITERS], const FwdArgs& a,
+                                        int64_t step, const Lane& L, float (*red)[kMaxBlockWaves], Rsrc rr,
+                                        uint32_t voff, uint32_t iter_bytes, uint32_t row_bytes) {
+  const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
+  const bool active = row < a.M;
+  S* y = static_cast<S*>(a.y);
+  const Rsrc ry = make_rsrc(y + (active ? row * a.stride : 0), active ? row_bytes : 0u);
+
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float f = xv[i].get(e);
+      ss = fmaf(f, f, ss);
+    }
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) xv[i].keep_packed();
+  ss = wave_sum(ss);
+  if (a.wpr > 1) ss = group_sum(ss, red, step, L.wave, L.group, a.wpr, L.lane);
+
+  // mean over the true N (not a padded width), eps under the root
+  const float r = rsqrtf(fmaf(ss, a.inv_n, a.eps));
+  // one lane per row writes r; every other lane's offset is out of range
+  const bool writer = active && L.wv == 0 && L.lane == 0;
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r), rr,
+                                        writer ? static_cast<uint32_t>(row) * 4u : kOutOfRange, 0, kDefault);
+
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float normed = xv[i].get(e) * r;
+      if (a.round_normed) normed = round_to<S>(normed);  // uniform branch
+      o[e] = normed * (gv[i].get(e) + a.w_off);
+    }
+    buf_store<S, VEC, kFwdStoreY>(round_pack<S, VEC>(o), ry, voff + i * iter_bytes);
+  }
+}
+
+template <typename S, int VEC, int ITERS, bool EARLY>
 __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
   constexpr uint32_t kPack = Pack<S, VEC>::kBytes;
   const Lane L(a.wpr);
@@ -86,55 +130,40 @@ __global__ __launch_bounds__(1024) void rmsnorm_fwd_kernel(const FwdArgs a) {
   const Rsrc rg = make_rsrc(a.gamma, row_bytes);
   const Rsrc rr = make_rsrc(a.rstd, static_cast<uint32_t>(a.M) * 4u);
   const S* x = static_cast<const S*>(a.x);
-  S* y = static_cast<S*>(a.y);
 
   // gamma once per workgroup (the same columns for every row it takes)
   Pack<S, VEC> gv[ITERS];
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) gv[i] = buf_load<S, VEC, kDefault>(rg, voff + i * iter_bytes);
 
-  for (int64_t step = 0; step < a.row_iters; ++step) {
+  // row `step`'s x, all of this lane's loads before any arithmetic
+  auto load_row = [&](Pack<S, VEC>(&xv)[ITERS], int64_t step) {
     const int64_t row = row_of(step, a.row_iters, a.rpb, L.group);
     const bool active = row < a.M;
-    const int64_t off = active ? row * a.stride : 0;
-    const Rsrc rx = make_rsrc(x + off, active ? row_bytes : 0u);
-    const Rsrc ry = make_rsrc(y + off, active ? row_bytes : 0u);
-
-    // all of this lane's loads for the row before any arithmetic
-    Pack<S, VEC> xv[ITERS];
+    const Rsrc rx = make_rsrc(x + (active ? row * a.stride : 0), active ? row_bytes : 0u);
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) xv[i] = buf_load<S, VEC, kFwdLoadX>(rx, voff + i * iter_bytes);
+  };
 
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float f = xv[i].get(e);
-        ss = fmaf(f, f, ss);
-      }
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) xv[i].keep_packed();
-    ss = wave_sum(ss);
-    if (a.wpr > 1) ss = group_sum(ss, red, step, L.wave, L.group, a.wpr, L.lane);
-
-    // mean over the true N (not a padded width), eps under the root
-    const float r = rsqrtf(fmaf(ss, a.inv_n, a.eps));
-    // one lane per row writes r; every other lane's offset is out of range
-    const bool writer = active && L.wv == 0 && L.lane == 0;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, r), rr,
-                                          writer ? static_cast<uint32_t>(row) * 4u : kOutOfRange, 0, kDefault);
-
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      float o[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float normed = xv[i].get(e) * r;
-        if (a.round_normed) normed = round_to<S>(normed);  // uniform branch
-        o[e] = normed * (gv[i].get(e) + a.w_off);
-      }
-      buf_store<S, VEC, kFwdStoreY>(round_pack<S, VEC>(o), ry, voff + i * iter_bytes);
+  Pack<S, VEC> xv[ITERS];
+  if constexpr (EARLY) {
+    // The first row's loads go out before anything waits for gamma: the
+    // weight's unpacking, which the compiler hoists out of the row loop, then
+    // waits for gamma alone with the row's loads in flight.  Each step then
+    // loads the next row, if there is one, after storing its own (a load of a
+    // row past the last step, even one that reads nothing, keeps a one-step
+    // workgroup alive for its round trip).
+    load_row(xv, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t step = 0; step < a.row_iters; ++step) {
+      fwd_row(xv, gv, a, step, L, red, rr, voff, iter_bytes, row_bytes);
+      if (step + 1 < a.row_iters) load_row(xv, step + 1);
+    }
+  } else {
+    // Load a row, then work on it.
+    for (int64_t step = 0; step < a.row_iters; ++step) {
+      load_row(xv, step);
+      fwd_row(xv, gv, a, step, L, red, rr, voff, iter_bytes, row_bytes);
     }
   }
 }
@@ -396,8 +425,18 @@ hipError_t fwd_inst(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
   if constexpr (VEC * ITERS > lane_elems_cap(RowOp::kRmsFwd, sizeof(S))) {
     return hipErrorInvalidValue;  // beyond the register model: never planned, not compiled
   } else {
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<S, VEC, ITERS>), dim3(static_cast<unsigned>(p.grid)), dim3(p.threads()), 0, s,
-                       a);
+    // The first row's loads ahead of the weight's unpacking: compiled for
+    // 16-byte vectors and at most 8 per lane (with 16 the early row's
+    // registers spill), and launched where the plan asks for it.
+    if constexpr (VEC * sizeof(S) == 16 && ITERS <= 8) {
+      if (a.first_row_early) {
+        hipLaunchKernelGGL((rmsnorm_fwd_kernel<S, VEC, ITERS, true>), dim3(static_cast<unsigned>(p.grid)),
+                           dim3(p.threads()), 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<S, VEC, ITERS, false>), dim3(static_cast<unsigned>(p.grid)),
+                       dim3(p.threads()), 0, s, a);
     return hipGetLastError();
   }
 }
