@@ -177,8 +177,9 @@ int main(int argc, char** argv) {
     }
   }
   // grids the planner's rules pick, 16-byte vectors: (element size, M, N,
-  // op, dtype, workgroups, row groups per workgroup, row steps, pipelined
-  // backward: 1 / 0, -1 for a forward)
+  // op, dtype, workgroups, row groups per workgroup, row steps, and 1 / 0:
+  // the backward pipelined, the RMSNorm forward's first row loaded early;
+  // -1 for the LayerNorm forward)
   struct GridPin {
     int es;
     int64_t M, N;
@@ -207,27 +208,34 @@ int main(int argc, char** argv) {
       // forward of 3-6 row steps (LayerNorm; 3-4 RMSNorm): 1024 workgroups of
       // one row group, for rows of >= 7 KiB and <= 5 waves
       {2, 4096, 4096, RowOp::kLnFwd, 2, 1024, 1, 4, -1},
-      {2, 4096, 4096, RowOp::kRmsFwd, 1, 1024, 1, 4, -1},
+      {2, 4096, 4096, RowOp::kRmsFwd, 1, 1024, 1, 4, 1},
       {2, 6000, 5632, RowOp::kLnFwd, 2, 1024, 1, 6, -1},
-      {2, 2049, 3584, RowOp::kRmsFwd, 1, 1024, 1, 3, -1},
-      {2, 6000, 4096, RowOp::kRmsFwd, 1, 3000, 2, 1, -1},    // 6 steps: RMSNorm keeps the other rules
+      {2, 2049, 3584, RowOp::kRmsFwd, 1, 1024, 1, 3, 1},
+      {2, 6000, 4096, RowOp::kRmsFwd, 1, 3000, 2, 1, 0},        // 6 steps: RMSNorm keeps the other rules
       // ... and rows of 2-7 KiB where the rows divide evenly into 2-6 steps
       // (2-4 RMSNorm) over a whole number of workgroups per CU, at most four
       {2, 4096, 3072, RowOp::kLnFwd, 2, 1024, 2, 2, -1},     // 3-wave rows, two per workgroup
-      {2, 4096, 3328, RowOp::kRmsFwd, 1, 1024, 2, 2, -1},    // 4-wave rows
+      {2, 4096, 3328, RowOp::kRmsFwd, 1, 1024, 2, 2, 1},        // 4-wave rows
       {2, 12288, 2816, RowOp::kLnFwd, 2, 1024, 2, 6, -1},
-      {2, 12288, 2816, RowOp::kRmsFwd, 1, 6144, 2, 1, -1},   // 6 steps: RMSNorm keeps the other rules
+      {2, 12288, 2816, RowOp::kRmsFwd, 1, 6144, 2, 1, 0},       // 6 steps: RMSNorm keeps the other rules
       {2, 6144, 2304, RowOp::kLnFwd, 2, 768, 4, 2, -1},      // 1-wave rows, four per workgroup
-      {2, 16384, 2048, RowOp::kRmsFwd, 1, 1024, 4, 4, -1},   // 2-wave rows
+      {2, 16384, 2048, RowOp::kRmsFwd, 1, 1024, 4, 4, 1},       // 2-wave rows
       {2, 5000, 3072, RowOp::kLnFwd, 2, 2500, 2, 1, -1},     // rows that do not divide evenly
       {2, 8192, 1024, RowOp::kLnFwd, 2, 1024, 8, 1, -1},     // 2 KiB rows
+      // the RMSNorm forward's first row loaded early: persistent grids and
+      // grids of at most 2048 workgroups, not large one-step grids
+      {2, 16384, 8192, RowOp::kRmsFwd, 1, 512, 1, 32, 1},    // the headline
+      {2, 4096, 2048, RowOp::kRmsFwd, 1, 1024, 4, 1, 1},
+      {2, 32768, 5120, RowOp::kRmsFwd, 1, 32768, 1, 1, 0},
       {2, 4096, 12288, RowOp::kLnFwd, 2, 512, 1, 8, -1},     // 6-wave rows of four vectors: persistent, two per CU
       {2, 2048, 6144, RowOp::kLnFwd, 2, 1024, 2, 1, -1},     // 2 steps: one workgroup per two 3 x 4 row groups
   };
   for (const GridPin& q : grid_pins) {
     const RowPlan p = plan_rows(q.op, q.M, q.N, 16 / q.es, q.dtype);
     ++n;
-    const int pipe = q.op == RowOp::kRmsBwd || q.op == RowOp::kLnBwd ? int(bwd_pipelined(q.op, p, q.dtype)) : -1;
+    const int pipe = q.op == RowOp::kRmsBwd || q.op == RowOp::kLnBwd ? int(bwd_pipelined(q.op, p, q.dtype))
+                     : q.op == RowOp::kRmsFwd                          ? int(fwd_first_row_early(p))
+                                                                       : -1;
     if (p.grid != q.grid || p.rpb != q.rpb || p.row_iters != q.row_iters || pipe != q.pipelined) {
       ++bad;
       std::printf("grid pin: op=%d dtype=%d %ld x %ld: got grid %ld, %d row groups, %ld steps, pipelined %d; expected "
