@@ -89,7 +89,8 @@ __global__ __launch_bounds__(1024) void layernorm_fwd_kernel(const LnFwdArgs a) 
     // weight and bias are unpacked inside the loop, after the row's loads
     // are issued: unpacked before it, the first row's x loads wait for them
     // (measured 7-14 % slower at 4096 x 10240 and 4096 x 12288 fp16).  The
-    // RMSNorm forward, with one operand less, measured the other way.
+    // RMSNorm forward, with one operand less, keeps its weight unpacked
+    // across the rows and issues the first row's loads ahead of that instead.
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
       wv[i].keep_packed();
