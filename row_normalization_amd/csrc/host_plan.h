@@ -334,7 +334,9 @@ inline void plan_fwd_grid(RowPlan& p, RowOp op, int64_t M, int64_t N, int es) {
     return;
   }
   if (es == 2 && p.vec * es == 16 && N * es > kFwdFewStepsShortMinRowBytes && N * es < kFwdFewStepsMinRowBytes) {
-    // rows per CU and row step with one workgroup per CU
+    // One workgroup per CU covers cu_step_rows rows per row step; M holds
+    // `units` such blocks of rows (whole ones only), dealt out as `steps` row
+    // steps to units / steps workgroups per CU (at most four).
     const int rpb = std::max(1, std::min(kFwdFewStepsShortGroups, kBlockWaves / p.wpr));
     const int64_t cu_step_rows = int64_t(rpb) * kComputeUnits;
     const int64_t units = M / cu_step_rows;
