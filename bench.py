@@ -651,7 +651,7 @@ def cpu_baseline(w: wl.Workload, seconds: float, all_cores_seconds: float) -> di
 
 
 CEILING_PROBE = os.path.join(ROOT, "tests", "native", "bin", "stream_ceiling")
-CEILING_MIXES = ("read", "read1_write1", "read2_write1", "read2_write1_in_place")
+CEILING_MIXES = ("read", "read1_write1", "read2_write1", "read2_write1_in_place", "read3_write3")
 
 
 def stream_ceiling():
@@ -659,7 +659,8 @@ def stream_ceiling():
     operand) for the read/write mixes of the row kernels: read only, one read
     per write, two reads per write, and two reads per write in place (dx over
     dy), each the best over grid-stride and row-walk shapes, both cache
-    policies (tests/native/stream_ceiling.hip).  Run as a
+    policies, and three reads with three writes (the SwiGLU backward)
+    (tests/native/stream_ceiling.hip).  Run as a
     child process before this process touches the GPU.  None if the probe has
     not been built."""
     import subprocess
@@ -990,6 +991,11 @@ def main():
         torch.cuda.empty_cache()
         out["swiglu"] = swiglu_leg(args.samples)
         out["swiglu"]["traffic_bytes"] = {leg: traffic_tab.get(f"swiglu {leg}") for leg in ("fwd", "bwd")}
+        # each leg against the plain streaming rate of its own read/write mix
+        if ceiling and "read3_write3" in ceiling:
+            out["swiglu"]["vs_ceiling"] = {
+                "fwd_vs_read2_write1": round(out["swiglu"]["fwd_gbps"] / ceiling["read2_write1"]["hot_gbps"], 4),
+                "bwd_vs_read3_write3": round(out["swiglu"]["bwd_gbps"] / ceiling["read3_write3"]["hot_gbps"], 4)}
         print(f"[swiglu] {out['swiglu']}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -2,8 +2,10 @@
 // the row kernels, as the reference point for their HBM rooflines: read only,
 // one read per write (the forwards: x in, y out), two reads per write (the
 // backwards: x and dy in, dx out) and two reads per write in place (dx over
-// dy, as in the headline backward).  256 MiB per operand, the size of one
-// 16384 x 8192 bf16 tensor.  Every access is a 16-byte vector load or store.
+// dy, as in the headline backward), and three reads with three writes (the
+// elementwise SwiGLU backward).  256 MiB per
+// operand, the size of one 16384 x 8192 bf16 tensor.  Every access is a
+// 16-byte vector load or store.
 // The search covers, for every mix:
 //   * grid-stride loops: 32, 64 or 128 bytes of each input in flight per lane
 //     (2, 4 or 8 vectors), 256-, 512- and 1024-thread workgroups, grids of
@@ -88,6 +90,30 @@ __global__ void stream_kernel(const u32x4* a, const u32x4* b, u32x4* c, u32x4* _
   if (!WRITE) sink[first] = acc;  // keeps the loads; one vector per thread
 }
 
+// Three reads, three writes: grid-stride as stream_kernel (the same index
+// bounds), each output a different function of the three inputs.
+template <int UNROLL, bool NT>
+__global__ void stream3_kernel(const u32x4* a, const u32x4* b, const u32x4* c, u32x4* d, u32x4* e, u32x4* f,
+                               long n) {
+  const long stride = static_cast<long>(gridDim.x) * blockDim.x;
+  const long first = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (long i = first; i + (UNROLL - 1) * stride < n; i += UNROLL * stride) {
+    u32x4 v[UNROLL], w[UNROLL], x[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      v[u] = load<NT>(a + i + u * stride);
+      w[u] = load<NT>(b + i + u * stride);
+      x[u] = load<NT>(c + i + u * stride);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      store<NT>(d + i + u * stride, v[u] ^ w[u]);
+      store<NT>(e + i + u * stride, w[u] + x[u]);
+      store<NT>(f + i + u * stride, x[u] | v[u]);
+    }
+  }
+}
+
 // Row walk: rows of kRowVecs vectors (16 KiB), a T-thread workgroup covering
 // a row with kRowVecs / T vectors per lane, all of them loaded before any is
 // stored; workgroup b takes rows b, b + grid, ...  Every index is below
@@ -120,14 +146,37 @@ __global__ __launch_bounds__(T) void rows_kernel(const u32x4* a, const u32x4* b,
   if (!WRITE) sink[static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
 }
 
+// Three reads, three writes over the same row walk.
+template <int T, bool NT>
+__global__ __launch_bounds__(T) void rows3_kernel(const u32x4* a, const u32x4* b, const u32x4* c, u32x4* d, u32x4* e,
+                                                  u32x4* f, long rows) {
+  constexpr int kPer = kRowVecs / T;
+  for (long r = blockIdx.x; r < rows; r += gridDim.x) {
+    const long base = r * kRowVecs + threadIdx.x;
+    u32x4 v[kPer], w[kPer], x[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      v[u] = load<NT>(a + base + u * T);
+      w[u] = load<NT>(b + base + u * T);
+      x[u] = load<NT>(c + base + u * T);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      store<NT>(d + base + u * T, v[u] ^ w[u]);
+      store<NT>(e + base + u * T, w[u] + x[u]);
+      store<NT>(f + base + u * T, x[u] | v[u]);
+    }
+  }
+}
+
 struct Result {
   double hot = 0, cold = 0;
   char shape[64] = "";
   std::string all;  // "shape": hot GB/s, for every shape timed
 };
 
-// The four mixes: input count, whether the output is the second input.
-enum Mix { kRead, kCopy, kR2W1, kR2W1InPlace, kMixes };
+// The mixes: input count, output count, whether the output is the second input.
+enum Mix { kRead, kCopy, kR2W1, kR2W1InPlace, kR3W3, kMixes };
 
 int main() {
   const long bytes = 256L << 20;
@@ -136,10 +185,13 @@ int main() {
   const long flush_bytes = 1L << 30;
   const int grids[] = {256, 512, 1024, 2048, 4096};
   const int row_grids[] = {256, 512, 1024, 2048, 16384};
-  u32x4 *a, *b, *c, *sink, *flush;
+  u32x4 *a, *b, *c, *d, *e, *f, *sink, *flush;
   CHECK(hipMalloc(&a, bytes));
   CHECK(hipMalloc(&b, bytes));
   CHECK(hipMalloc(&c, bytes));
+  CHECK(hipMalloc(&d, bytes));
+  CHECK(hipMalloc(&e, bytes));
+  CHECK(hipMalloc(&f, bytes));
   // one vector per thread of the largest grid of either kind
   const long sink_vecs = std::max(4096L * 1024, 16384L * 1024);
   CHECK(hipMalloc(&sink, sink_vecs * 16));
@@ -147,6 +199,9 @@ int main() {
   CHECK(hipMemset(a, 1, bytes));
   CHECK(hipMemset(b, 2, bytes));
   CHECK(hipMemset(c, 0, bytes));
+  CHECK(hipMemset(d, 0, bytes));
+  CHECK(hipMemset(e, 0, bytes));
+  CHECK(hipMemset(f, 0, bytes));
   hipEvent_t t0, t1;
   CHECK(hipEventCreate(&t0));
   CHECK(hipEventCreate(&t1));
@@ -201,6 +256,7 @@ int main() {
     measure([&] { stream_kernel<U, 1, true, NT><<<g, bs>>>(a, b, c, sink, n); }, 2.0, res[kCopy], shape);
     measure([&] { stream_kernel<U, 2, true, NT><<<g, bs>>>(a, b, c, sink, n); }, 3.0, res[kR2W1], shape);
     measure([&] { stream_kernel<U, 2, true, NT><<<g, bs>>>(a, b, b, sink, n); }, 3.0, res[kR2W1InPlace], shape);
+    measure([&] { stream3_kernel<U, NT><<<g, bs>>>(a, b, c, d, e, f, n); }, 6.0, res[kR3W3], shape);
   };
   auto row_shapes = [&](auto t_tag, auto nt_tag, int g) {
     constexpr int T = decltype(t_tag)::value;
@@ -211,6 +267,7 @@ int main() {
     measure([&] { rows_kernel<T, 1, true, NT><<<g, T>>>(a, b, c, sink, rows); }, 2.0, res[kCopy], shape);
     measure([&] { rows_kernel<T, 2, true, NT><<<g, T>>>(a, b, c, sink, rows); }, 3.0, res[kR2W1], shape);
     measure([&] { rows_kernel<T, 2, true, NT><<<g, T>>>(a, b, b, sink, rows); }, 3.0, res[kR2W1InPlace], shape);
+    measure([&] { rows3_kernel<T, NT><<<g, T>>>(a, b, c, d, e, f, rows); }, 6.0, res[kR3W3], shape);
   };
   using nt = std::true_type;
   using dflt = std::false_type;
@@ -241,12 +298,15 @@ int main() {
   };
   std::printf(
       "{\"bytes_per_operand\": %ld, \"read\": %s, \"read1_write1\": %s, \"read2_write1\": %s, "
-      "\"read2_write1_in_place\": %s}\n",
+      "\"read2_write1_in_place\": %s, \"read3_write3\": %s}\n",
       bytes, obj(res[kRead]).c_str(), obj(res[kCopy]).c_str(), obj(res[kR2W1]).c_str(),
-      obj(res[kR2W1InPlace]).c_str());
+      obj(res[kR2W1InPlace]).c_str(), obj(res[kR3W3]).c_str());
   CHECK(hipFree(a));
   CHECK(hipFree(b));
   CHECK(hipFree(c));
+  CHECK(hipFree(d));
+  CHECK(hipFree(e));
+  CHECK(hipFree(f));
   CHECK(hipFree(sink));
   CHECK(hipFree(flush));
   return 0;

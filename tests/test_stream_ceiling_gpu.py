@@ -1,7 +1,7 @@
 """The streaming-ceiling probe bench.py reports beside the kernels
 (tests/native/stream_ceiling.hip) runs and prints one well-formed JSON line:
 for each read/write mix (read only, one read per write, two reads per write,
-two reads per write in place) a best hot and cold rate, the shape that gave it
+two reads per write in place, three reads with three writes) a best hot and cold rate, the shape that gave it
 and the rate of every shape timed."""
 import json
 import os
@@ -21,7 +21,7 @@ def test_probe_reports_every_mix():
     assert r.returncode == 0, r.stderr
     res = json.loads(r.stdout.strip().splitlines()[-1])
     assert res["bytes_per_operand"] == 256 << 20
-    for mix in ("read", "read1_write1", "read2_write1", "read2_write1_in_place"):
+    for mix in ("read", "read1_write1", "read2_write1", "read2_write1_in_place", "read3_write3"):
         m = res[mix]
         shapes = m["hot_gbps_by_shape"]
         assert m["best_hot_shape"] in shapes and m["hot_gbps"] == max(shapes.values())
